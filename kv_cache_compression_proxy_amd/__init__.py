@@ -1,0 +1,240 @@
+"""Python binding of libnq, the MI355X (gfx950) KV-cache compression hot path.
+
+Argument marshalling only: every step runs in the HIP kernels of ``libnq.so`` (built in-tree by
+``python -m kv_cache_compression_proxy_amd.build``). PyTorch supplies device memory and streams.
+Importing this package without the built library raises ImportError -- there is no fallback.
+
+Low-level functions carry the C names of ``include/nq.h`` (``nq_score_evict``, ``nq_encode``,
+``nq_decode``, ...) and take torch tensors. ``compress`` / ``decompress`` chain them with the
+pages' quality presets.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+from .presets import PRESETS, params_for
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      f"`python -m kv_cache_compression_proxy_amd.build` (no CPU fallback exists)")
+
+# torch ships its own HIP runtime; importing it first makes libnq's libamdhip64.so.7 dependency
+# resolve (by soname) to that same, already loaded runtime, so both share one device context.
+import torch  # noqa: E402,F401
+
+_lib = C.CDLL(LIB_PATH)
+
+NQ_OK, NQ_ERR_INVALID_ARG, NQ_ERR_UNSUPPORTED, NQ_ERR_WORKSPACE, NQ_ERR_HIP = 0, -1, -2, -3, -4
+NQ_OUT_F16, NQ_OUT_F32 = 0, 1
+EXPORTED = ("nq_keep_count", "nq_check_params", "nq_score_evict_workspace_bytes",
+            "nq_decode_workspace_bytes", "nq_attend_workspace_bytes", "nq_rope_table",
+            "nq_score_evict", "nq_encode", "nq_decode", "nq_attend_decode", "nq_status_string")
+
+
+class NqParams(C.Structure):
+    _fields_ = [("layers", C.c_int32), ("kv_heads", C.c_int32), ("tokens", C.c_int32),
+                ("head_dim", C.c_int32), ("layer_begin", C.c_int32), ("layer_end", C.c_int32),
+                ("window", C.c_int32), ("evict_permille", C.c_int32), ("bits_k", C.c_int32),
+                ("bits_v", C.c_int32), ("rope_base", C.c_double)]
+
+    def __repr__(self):
+        return "NqParams(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+_P = C.POINTER(NqParams)
+_v = C.c_void_p
+_sig = {
+    "nq_keep_count": (C.c_int32, [_P]),
+    "nq_check_params": (C.c_int, [_P]),
+    "nq_score_evict_workspace_bytes": (C.c_size_t, [_P]),
+    "nq_decode_workspace_bytes": (C.c_size_t, [_P]),
+    "nq_attend_workspace_bytes": (C.c_size_t, [_P, C.c_int32, C.c_int32]),
+    "nq_rope_table": (C.c_int, [_P, _v, _v, _v]),
+    "nq_score_evict": (C.c_int, [_P, _v, _v, _v, _v, C.c_size_t, _v]),
+    "nq_encode": (C.c_int, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v]),
+    "nq_decode": (C.c_int, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, C.c_int, _v, C.c_size_t, _v]),
+    "nq_attend_decode": (C.c_int, [_P, _v, C.c_int32, _v, _v, C.c_int32, _v, _v, C.c_size_t,
+                                   _v]),
+    "nq_status_string": (C.c_char_p, [C.c_int]),
+}
+for _name, (_res, _args) in _sig.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class NqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {_lib.nq_status_string(status).decode()} ({status})")
+        self.status = status
+
+
+def _ok(fn: str, status: int):
+    if status != NQ_OK:
+        raise NqError(fn, status)
+
+
+def _ptr(t):
+    """Device (or host) address of a tensor, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def make_params(layers, kv_heads, tokens, window, evict_permille, bits_k, bits_v, rope_base,
+                layer_begin=0, layer_end=None, head_dim=128) -> NqParams:
+    return NqParams(layers, kv_heads, tokens, head_dim, layer_begin,
+                    layers if layer_end is None else layer_end, window, evict_permille, bits_k,
+                    bits_v, float(rope_base))
+
+
+# ---------------------------------------------------------------- C entry points (same names)
+def nq_keep_count(p: NqParams) -> int:
+    return _lib.nq_keep_count(C.byref(p))
+
+
+def nq_check_params(p: NqParams) -> int:
+    return _lib.nq_check_params(C.byref(p))
+
+
+def nq_score_evict_workspace_bytes(p: NqParams) -> int:
+    return _lib.nq_score_evict_workspace_bytes(C.byref(p))
+
+
+def nq_decode_workspace_bytes(p: NqParams) -> int:
+    return _lib.nq_decode_workspace_bytes(C.byref(p))
+
+
+def nq_attend_workspace_bytes(p: NqParams, q_heads: int, n_tok: int) -> int:
+    return _lib.nq_attend_workspace_bytes(C.byref(p), q_heads, n_tok)
+
+
+def nq_rope_table(p, cos, sin, stream=None):
+    _ok("nq_rope_table", _lib.nq_rope_table(C.byref(p), _ptr(cos), _ptr(sin), _stream(stream)))
+
+
+def nq_score_evict(p, K, positions, workspace, scores=None, stream=None):
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _ok("nq_score_evict", _lib.nq_score_evict(C.byref(p), _ptr(K), _ptr(positions), _ptr(scores),
+                                              _ptr(workspace), ws, _stream(stream)))
+
+
+def nq_encode(p, K, V, positions, rope_cos, rope_sin, codes_k, codes_v, scales_k, scales_v,
+              stream=None):
+    _ok("nq_encode", _lib.nq_encode(C.byref(p), _ptr(K), _ptr(V), _ptr(positions), _ptr(rope_cos),
+                                    _ptr(rope_sin), _ptr(codes_k), _ptr(codes_v), _ptr(scales_k),
+                                    _ptr(scales_v), _stream(stream)))
+
+
+def nq_decode(p, codes_k, codes_v, scales_k, scales_v, positions, rope_cos, rope_sin, K_out,
+              V_out, out_dtype, workspace, stream=None):
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _ok("nq_decode", _lib.nq_decode(C.byref(p), _ptr(codes_k), _ptr(codes_v), _ptr(scales_k),
+                                    _ptr(scales_v), _ptr(positions), _ptr(rope_cos),
+                                    _ptr(rope_sin), _ptr(K_out), _ptr(V_out), out_dtype,
+                                    _ptr(workspace), ws, _stream(stream)))
+
+
+def nq_attend_decode(p, Q, q_heads, K, V, n_tok, out, workspace, stream=None):
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _ok("nq_attend_decode", _lib.nq_attend_decode(C.byref(p), _ptr(Q), q_heads, _ptr(K), _ptr(V),
+                                                  n_tok, _ptr(out), _ptr(workspace), ws,
+                                                  _stream(stream)))
+
+
+def nq_status_string(status: int) -> str:
+    return _lib.nq_status_string(status).decode()
+
+
+# ---------------------------------------------------------------- convenience chain
+@dataclass
+class Compressed:
+    params: NqParams
+    positions: "object"   # int32 [Lc, n_keep]
+    codes_k: "object"     # int8 [Lc, H, n_keep, 128] (delta-coded)
+    codes_v: "object"
+    scales_k: "object"    # fp16 [Lc, H, n_keep, 16]
+    scales_v: "object"
+    rope_cos: "object"    # fp32 [T, 64]
+    rope_sin: "object"
+
+    @property
+    def n_keep(self) -> int:
+        return self.positions.shape[1]
+
+
+def workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def rope_table(p: NqParams, device="cuda", stream=None):
+    import torch
+    cos = torch.empty((max(p.tokens, 1), 64), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    nq_rope_table(p, cos, sin, stream)
+    return cos, sin
+
+
+def compress(K, V, preset: str = "balanced", rope=None, stream=None, **overrides) -> Compressed:
+    """K, V: fp16 CUDA tensors [L, H, T, 128]. Runs scoring + eviction + encode on the GPU."""
+    import torch
+    L, H, T, D = K.shape
+    p = params_for(preset, L, H, T, **overrides)
+    _ok("nq_check_params", nq_check_params(p))
+    n_keep = nq_keep_count(p)
+    Lc = p.layer_end - p.layer_begin
+    dev = K.device
+    cos, sin = rope if rope is not None else rope_table(p, dev, stream)
+    positions = torch.empty((Lc, n_keep), dtype=torch.int32, device=dev)
+    ws = workspace(nq_score_evict_workspace_bytes(p), dev)
+    nq_score_evict(p, K, positions, ws, stream=stream)
+    ck = torch.empty((Lc, H, n_keep, 128), dtype=torch.int8, device=dev)
+    cv = torch.empty_like(ck)
+    sk = torch.empty((Lc, H, n_keep, 16), dtype=torch.float16, device=dev)
+    sv = torch.empty_like(sk)
+    nq_encode(p, K, V, positions, cos, sin, ck, cv, sk, sv, stream)
+    return Compressed(p, positions, ck, cv, sk, sv, cos, sin)
+
+
+def decompress(c: Compressed, out_dtype=None, stream=None):
+    """-> (K_hat, V_hat) [Lc, H, n_keep, 128] in fp16 (default) or fp32."""
+    import torch
+    out_dtype = out_dtype or torch.float16
+    Lc, H, n, _ = c.codes_k.shape
+    Ko = torch.empty((Lc, H, n, 128), dtype=out_dtype, device=c.codes_k.device)
+    Vo = torch.empty_like(Ko)
+    ws = workspace(nq_decode_workspace_bytes(c.params), c.codes_k.device)
+    nq_decode(c.params, c.codes_k, c.codes_v, c.scales_k, c.scales_v, c.positions, c.rope_cos,
+              c.rope_sin, Ko, Vo, NQ_OUT_F32 if out_dtype == torch.float32 else NQ_OUT_F16, ws,
+              stream)
+    return Ko, Vo
+
+
+def attend(c_params: NqParams, Q, K_hat, V_hat, stream=None):
+    """One-token GQA over a reconstructed cache: Q fp16 [Lc, Hq, 128] -> fp32 [Lc, Hq, 128]."""
+    import torch
+    Lc, Hq, _ = Q.shape
+    n = K_hat.shape[2]
+    out = torch.empty((Lc, Hq, 128), dtype=torch.float32, device=Q.device)
+    ws = workspace(nq_attend_workspace_bytes(c_params, Hq, n), Q.device)
+    nq_attend_decode(c_params, Q, Hq, K_hat, V_hat, n, out, ws, stream)
+    return out
+
+
+__all__ = ["NqParams", "NqError", "Compressed", "PRESETS", "params_for", "make_params",
+           "compress", "decompress", "attend", "rope_table", "workspace", *EXPORTED]

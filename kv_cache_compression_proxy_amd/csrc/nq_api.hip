@@ -1,0 +1,360 @@
+// libnq host side: the C ABI declared in include/nq.h -- argument validation, workspace
+// layout and kernel launches on the caller's stream. No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "nq.h"
+#include "nq_attend.hpp"
+#include "nq_codec.hpp"
+#include "nq_score.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+int32_t compressed_layers(const nq_params *p) { return p->layer_end - p->layer_begin; }
+
+nq_status check(const nq_params *p)
+{
+    if (!p) return NQ_ERR_INVALID_ARG;
+    if (p->layers < 1 || p->kv_heads < 1 || p->tokens < 0 || p->head_dim < 1)
+        return NQ_ERR_INVALID_ARG;
+    if (p->layer_begin < 0 || p->layer_end < p->layer_begin || p->layer_end > p->layers)
+        return NQ_ERR_INVALID_ARG;
+    if (p->window < 0 || p->evict_permille < 0 || p->evict_permille > 1000)
+        return NQ_ERR_INVALID_ARG;
+    if (p->bits_k < 2 || p->bits_v < 2 || !(p->rope_base > 1.0) || !isfinite(p->rope_base))
+        return NQ_ERR_INVALID_ARG;
+    if (p->head_dim != 128) return NQ_ERR_UNSUPPORTED;
+    if (p->bits_k > 4 || p->bits_v > 4) return NQ_ERR_UNSUPPORTED;
+    // 32-bit token and tile indices inside the kernels
+    if ((int64_t)p->tokens * 16 > INT32_MAX) return NQ_ERR_UNSUPPORTED;
+    if ((int64_t)p->kv_heads * 2 * compressed_layers(p) * ((int64_t)p->tokens / nq::kCodecTile + 1) >
+        INT32_MAX)
+        return NQ_ERR_UNSUPPORTED;
+    return NQ_OK;
+}
+
+int32_t keep_count(const nq_params *p)
+{
+    const int64_t T = p->tokens;
+    if (T <= 0) return 0;
+    const int64_t n_evict = (int64_t)p->evict_permille * T / 1000;
+    const int64_t prot = (int64_t)p->window + 1 < T ? (int64_t)p->window + 1 : T;
+    const int64_t keep = T - n_evict;
+    return (int32_t)(keep > prot ? keep : prot);
+}
+
+float rho_of(int bits) { return (float)((1 << (bits - 1)) - 1); }
+
+// An error left by an earlier, unrelated runtime call must not be reported as ours: entry
+// points clear the thread's last error before they launch, then read it after.
+void clear_error() { (void)hipGetLastError(); }
+
+nq_status launched(const char *fn)
+{
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) return NQ_OK;
+    if (getenv("NQ_VERBOSE")) fprintf(stderr, "libnq %s: %s\n", fn, hipGetErrorString(e));
+    return NQ_ERR_HIP;
+}
+
+struct ScoreWs {
+    double *qbar, *scores;
+    size_t bytes;
+};
+
+ScoreWs score_ws(const nq_params *p, void *base)
+{
+    const size_t Lc = (size_t)compressed_layers(p);
+    const size_t qb = align_up(Lc * p->kv_heads * 128 * sizeof(double));
+    const size_t sc = align_up(Lc * (size_t)p->tokens * sizeof(double));
+    ScoreWs w;
+    w.qbar = (double *)base;
+    w.scores = (double *)((char *)base + qb);
+    w.bytes = qb + sc;
+    return w;
+}
+
+int32_t codec_tiles(const nq_params *p) { return (keep_count(p) + nq::kCodecTile - 1) / nq::kCodecTile; }
+
+struct DecodeWs {
+    uint32_t *flag, *ticket;
+    uint2 *agg, *incl;
+    size_t bytes;
+    int32_t tiles;
+};
+
+DecodeWs decode_ws(const nq_params *p, void *base)
+{
+    DecodeWs w;
+    w.tiles = compressed_layers(p) * 2 * p->kv_heads * codec_tiles(p);
+    const size_t nt = (size_t)w.tiles;
+    const size_t f = align_up((nt + 1) * sizeof(uint32_t));
+    const size_t t = align_up(2 * sizeof(uint32_t));
+    const size_t v = align_up(nt * 16 * sizeof(uint2));
+    char *b = (char *)base;
+    w.flag = (uint32_t *)b;
+    w.ticket = (uint32_t *)(b + f);
+    w.agg = (uint2 *)(b + f + t);
+    w.incl = (uint2 *)(b + f + t + v);
+    w.bytes = f + t + 2 * v;
+    return w;
+}
+
+int attend_nsplit(const nq_params *p, int32_t n_tok)
+{
+    // aim for >= ~2048 blocks in total, chunks of >= 256 tokens
+    const int64_t lh = (int64_t)compressed_layers(p) * p->kv_heads;
+    int64_t ns = (2048 + lh - 1) / (lh > 0 ? lh : 1);
+    const int64_t max_by_len = (n_tok + 255) / 256;
+    if (ns > max_by_len) ns = max_by_len;
+    if (ns < 1) ns = 1;
+    return (int)ns;
+}
+
+struct AttWs {
+    float *m, *l, *acc;
+    size_t bytes;
+    int nsplit;
+};
+
+AttWs attend_ws(const nq_params *p, int32_t q_heads, int32_t n_tok, void *base)
+{
+    AttWs w;
+    w.nsplit = attend_nsplit(p, n_tok);
+    const size_t G = (size_t)(q_heads / p->kv_heads);
+    const size_t blocks = (size_t)compressed_layers(p) * p->kv_heads * w.nsplit;
+    const size_t a = align_up(blocks * G * sizeof(float));
+    const size_t c = align_up(blocks * G * 128 * sizeof(float));
+    w.m = (float *)base;
+    w.l = (float *)((char *)base + a);
+    w.acc = (float *)((char *)base + 2 * a);
+    w.bytes = 2 * a + c;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nq_keep_count(const nq_params *p)
+{
+    if (check(p) != NQ_OK) return -1;
+    return keep_count(p);
+}
+
+nq_status nq_check_params(const nq_params *p) { return check(p); }
+
+size_t nq_score_evict_workspace_bytes(const nq_params *p)
+{
+    if (check(p) != NQ_OK) return 0;
+    return score_ws(p, nullptr).bytes;
+}
+
+size_t nq_decode_workspace_bytes(const nq_params *p)
+{
+    if (check(p) != NQ_OK) return 0;
+    return decode_ws(p, nullptr).bytes;
+}
+
+size_t nq_attend_workspace_bytes(const nq_params *p, int32_t q_heads, int32_t n_tok)
+{
+    if (check(p) != NQ_OK || q_heads < 1 || n_tok < 0 || q_heads % p->kv_heads) return 0;
+    return attend_ws(p, q_heads, n_tok, nullptr).bytes;
+}
+
+const char *nq_status_string(nq_status s)
+{
+    switch (s) {
+    case NQ_OK: return "ok";
+    case NQ_ERR_INVALID_ARG: return "invalid argument";
+    case NQ_ERR_UNSUPPORTED: return "unsupported parameters";
+    case NQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case NQ_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+nq_status nq_rope_table(const nq_params *p, float *cos_dev, float *sin_dev, void *stream)
+{
+    nq_status st = check(p);
+    if (st != NQ_OK) return st;
+    if (p->tokens == 0) return NQ_OK;
+    if (!cos_dev || !sin_dev || !aligned(cos_dev, 16) || !aligned(sin_dev, 16))
+        return NQ_ERR_INVALID_ARG;
+    nq::RopeTheta th;
+    for (int i = 0; i < 64; i++) th.v[i] = pow(p->rope_base, -(double)i / 64.0);
+    const int64_t n = (int64_t)p->tokens * 64;
+    clear_error();
+    hipLaunchKernelGGL(nq::k_rope_table, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0,
+                       as_stream(stream), th, p->tokens, cos_dev, sin_dev);
+    return launched("nq_rope_table");
+}
+
+nq_status nq_score_evict(const nq_params *p, const void *K, int32_t *positions,
+                         double *scores_opt, void *workspace, size_t ws_bytes, void *stream)
+{
+    nq_status st = check(p);
+    if (st != NQ_OK) return st;
+    const int32_t Lc = compressed_layers(p), T = p->tokens, H = p->kv_heads;
+    const int32_t n_keep = keep_count(p);
+    if (Lc == 0 || T == 0) return NQ_OK;
+    if (!K || !positions || !aligned(K, 16) || !aligned(positions, 4)) return NQ_ERR_INVALID_ARG;
+    if (scores_opt && !aligned(scores_opt, 8)) return NQ_ERR_INVALID_ARG;
+    const size_t need = score_ws(p, nullptr).bytes;
+    if (!workspace || ws_bytes < need || !aligned(workspace, kAlign)) return NQ_ERR_WORKSPACE;
+    ScoreWs w = score_ws(p, workspace);
+    double *scores = scores_opt ? scores_opt : w.scores;
+    hipStream_t s = as_stream(stream);
+    const uint16_t *K16 = (const uint16_t *)K;
+    clear_error();
+    hipLaunchKernelGGL(nq::k_window_sum, dim3(Lc * H), dim3(256), 0, s, K16, H, T, p->window,
+                       p->layer_begin, w.qbar);
+    const int tiles = (T + nq::kScoreTile - 1) / nq::kScoreTile;
+    hipLaunchKernelGGL(nq::k_scores, dim3(Lc * tiles), dim3(256), 0, s, K16, w.qbar, H, T,
+                       p->window, p->layer_begin, tiles, scores);
+    hipLaunchKernelGGL(nq::k_select, dim3(Lc), dim3(nq::kSelThreads), 0, s, scores, T,
+                       p->window, n_keep, positions);
+    return launched("nq_score_evict");
+}
+
+static nq::CodecArgs codec_args(const nq_params *p, const int32_t *positions,
+                                const float *rope_cos, const float *rope_sin)
+{
+    nq::CodecArgs a;
+    memset(&a, 0, sizeof(a));
+    a.positions = positions;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
+    a.H = p->kv_heads;
+    a.T = p->tokens;
+    a.layer_begin = p->layer_begin;
+    a.n_keep = keep_count(p);
+    a.tiles_per_chain = codec_tiles(p);
+    a.rho_k = rho_of(p->bits_k);
+    a.rho_v = rho_of(p->bits_v);
+    return a;
+}
+
+nq_status nq_encode(const nq_params *p, const void *K, const void *V, const int32_t *positions,
+                    const float *rope_cos, const float *rope_sin, int8_t *codes_k,
+                    int8_t *codes_v, void *scales_k, void *scales_v, void *stream)
+{
+    nq_status st = check(p);
+    if (st != NQ_OK) return st;
+    const int32_t Lc = compressed_layers(p);
+    if (Lc == 0 || p->tokens == 0) return NQ_OK;
+    const void *ptrs16[] = {K, V, rope_cos, rope_sin, codes_k, codes_v};
+    for (const void *q : ptrs16)
+        if (!q || !aligned(q, 16)) return NQ_ERR_INVALID_ARG;
+    if (!positions || !aligned(positions, 4) || !scales_k || !scales_v || !aligned(scales_k, 4) ||
+        !aligned(scales_v, 4))
+        return NQ_ERR_INVALID_ARG;
+    nq::CodecArgs a = codec_args(p, positions, rope_cos, rope_sin);
+    a.K = (const uint16_t *)K;
+    a.V = (const uint16_t *)V;
+    a.codes_k = codes_k;
+    a.codes_v = codes_v;
+    a.scales_k = (uint16_t *)scales_k;
+    a.scales_v = (uint16_t *)scales_v;
+    const int64_t blocks = (int64_t)Lc * 2 * p->kv_heads * a.tiles_per_chain;
+    clear_error();
+    hipLaunchKernelGGL(nq::k_encode, dim3((uint32_t)blocks), dim3(nq::kCodecThreads), 0,
+                       as_stream(stream), a);
+    return launched("nq_encode");
+}
+
+nq_status nq_decode(const nq_params *p, const int8_t *codes_k, const int8_t *codes_v,
+                    const void *scales_k, const void *scales_v, const int32_t *positions,
+                    const float *rope_cos, const float *rope_sin, void *K_out, void *V_out,
+                    nq_out_dtype out_dtype, void *workspace, size_t ws_bytes, void *stream)
+{
+    nq_status st = check(p);
+    if (st != NQ_OK) return st;
+    if (out_dtype != NQ_OUT_F16 && out_dtype != NQ_OUT_F32) return NQ_ERR_INVALID_ARG;
+    const int32_t Lc = compressed_layers(p);
+    if (Lc == 0 || p->tokens == 0) return NQ_OK;
+    const void *ptrs16[] = {codes_k, codes_v, rope_cos, rope_sin, K_out, V_out};
+    for (const void *q : ptrs16)
+        if (!q || !aligned(q, 16)) return NQ_ERR_INVALID_ARG;
+    if (!positions || !aligned(positions, 4) || !scales_k || !scales_v || !aligned(scales_k, 4) ||
+        !aligned(scales_v, 4))
+        return NQ_ERR_INVALID_ARG;
+    const size_t need = decode_ws(p, nullptr).bytes;
+    if (!workspace || ws_bytes < need || !aligned(workspace, kAlign)) return NQ_ERR_WORKSPACE;
+    DecodeWs w = decode_ws(p, workspace);
+    nq::CodecArgs a = codec_args(p, positions, rope_cos, rope_sin);
+    a.codes_k = (int8_t *)codes_k;
+    a.codes_v = (int8_t *)codes_v;
+    a.scales_k = (uint16_t *)scales_k;
+    a.scales_v = (uint16_t *)scales_v;
+    a.out_k = K_out;
+    a.out_v = V_out;
+    a.out_f32 = out_dtype == NQ_OUT_F32;
+    a.lb_flag = w.flag;
+    a.lb_ticket = w.ticket;
+    a.lb_agg = w.agg;
+    a.lb_incl = w.incl;
+    hipStream_t s = as_stream(stream);
+    clear_error();
+    hipLaunchKernelGGL(nq::k_decode_reset, dim3((w.tiles + 255) / 256 + 1), dim3(256), 0, s,
+                       w.flag, w.tiles, w.ticket);
+    hipLaunchKernelGGL(nq::k_decode, dim3((uint32_t)w.tiles), dim3(nq::kCodecThreads), 0, s, a);
+    return launched("nq_decode");
+}
+
+nq_status nq_attend_decode(const nq_params *p, const void *Q, int32_t q_heads, const void *K,
+                           const void *V, int32_t n_tok, float *out, void *workspace,
+                           size_t ws_bytes, void *stream)
+{
+    nq_status st = check(p);
+    if (st != NQ_OK) return st;
+    if (q_heads < 1 || n_tok < 0 || q_heads % p->kv_heads) return NQ_ERR_INVALID_ARG;
+    const int G = q_heads / p->kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return NQ_ERR_UNSUPPORTED;
+    const int32_t Lc = compressed_layers(p);
+    if (Lc == 0) return NQ_OK;
+    const void *ptrs16[] = {Q, K, V, out};
+    for (const void *q : ptrs16)
+        if (!q || !aligned(q, 16)) return NQ_ERR_INVALID_ARG;
+    const size_t need = attend_ws(p, q_heads, n_tok, nullptr).bytes;
+    if (!workspace || ws_bytes < need || !aligned(workspace, kAlign)) return NQ_ERR_WORKSPACE;
+    AttWs w = attend_ws(p, q_heads, n_tok, workspace);
+    nq::AttArgs a;
+    a.Q = (const uint16_t *)Q;
+    a.K = (const uint16_t *)K;
+    a.V = (const uint16_t *)V;
+    a.out = out;
+    a.part_m = w.m;
+    a.part_l = w.l;
+    a.part_acc = w.acc;
+    a.H = p->kv_heads;
+    a.Hq = q_heads;
+    a.n = n_tok;
+    a.nsplit = w.nsplit;
+    hipStream_t s = as_stream(stream);
+    const dim3 grid((uint32_t)(Lc * p->kv_heads * w.nsplit));
+    clear_error();
+    switch (G) {
+    case 1: hipLaunchKernelGGL(nq::k_attend<1>, grid, dim3(nq::kAttThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(nq::k_attend<2>, grid, dim3(nq::kAttThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(nq::k_attend<4>, grid, dim3(nq::kAttThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(nq::k_attend<8>, grid, dim3(nq::kAttThreads), 0, s, a); break;
+    }
+    hipLaunchKernelGGL(nq::k_attend_merge, dim3((uint32_t)(Lc * q_heads)), dim3(128), 0, s, a, G);
+    return launched("nq_attend_decode");
+}
+
+}  // extern "C"

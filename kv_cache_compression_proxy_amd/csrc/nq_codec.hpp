@@ -1,0 +1,450 @@
+// Encode and decode kernels: RoPE removal/restore, 128-point Hadamard rotation, per-group fp16
+// scales, E8 nearest point, delta coding along the kept tokens and its running-sum inverse.
+//
+// Method: "Como comprimir o KV cache do seu LLM em 33x sem treino", section "Como funciona",
+// steps 3-6 (RoPE removal, Hadamard rotation, E8 quantization of 8-float groups, delta coding);
+// "NexusQuant：无需训练实现LLM KV缓存10-33倍压缩的技术突破", sections "E8格点量化" and
+// "技术实现细节" (keys 3-bit / values 2-bit; RoPE restored after quantization).
+//
+// Work decomposition (both directions). A chain is one (compressed layer, tensor K|V, kv head):
+// the delta code runs along its kept tokens. A 256-thread workgroup owns a tile of 16*R
+// consecutive kept tokens of one chain; each of its 16 lane groups walks R consecutive tokens
+// in order, so the previous token's code is still in registers when the next token is coded.
+#pragma once
+
+#include "nq_common.hpp"
+
+namespace nq {
+
+constexpr int kCodecThreads = 256;
+constexpr int kCodecRun = 16;                          // tokens walked per lane group
+constexpr int kCodecTile = 16 * kCodecRun;             // tokens per workgroup tile
+
+struct CodecArgs {
+    const uint16_t *K, *V;         // fp16 [L][H][T][128]
+    const int32_t *positions;      // [Lc][n_keep]
+    const float *rope_cos, *rope_sin;  // [T][64]
+    int8_t *codes_k, *codes_v;     // [Lc][H][n_keep][128]
+    uint16_t *scales_k, *scales_v; // fp16 bits [Lc][H][n_keep][16]
+    void *out_k, *out_v;           // decode outputs [Lc][H][n_keep][128]
+    uint32_t *lb_flag;             // decode look-back: per tile status (0 none, 1 agg, 2 incl)
+    uint2 *lb_agg, *lb_incl;       // [tiles][16] byte-wise sums of one tile / of its prefix
+    uint32_t *lb_ticket;           // [0]: tile ticket counter, [1]: spin-limit error flag
+    int32_t H, T, layer_begin, n_keep;
+    int32_t tiles_per_chain;
+    float rho_k, rho_v;
+    int32_t out_f32;
+};
+
+// Split-half rotary table: C[p][i] = fp32(cos(p * theta_i)), S[p][i] = fp32(sin(p * theta_i)),
+// angles in fp64 from theta_i = base^(-i/64) computed on the host.
+struct RopeTheta {
+    double v[64];
+};
+
+__global__ __launch_bounds__(256) void k_rope_table(RopeTheta th, int T, float *__restrict__ C,
+                                                   float *__restrict__ S)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)T * 64) return;
+    const int i = (int)(idx & 63);
+    const double phi = (double)(idx >> 6) * th.v[i];
+    double sv, cv;
+    sincos(phi, &sv, &cv);
+    C[idx] = (float)cv;
+    S[idx] = (float)sv;
+}
+
+// Normalised Hadamard transform of a row held as 8 values per lane (dims 8g + j), butterflies
+// in the order h = 1, 2, 4 (inside the lane) then 8, 16, 32, 64 (lane partners g^1, g^2, g^4,
+// g^8), pair (a, b) -> (a + b, a - b); then times fp32(1/sqrt(128)). Same fp32 results as the
+// sequential order: every butterfly output is one correctly rounded add or subtract.
+__device__ __forceinline__ void hadamard_rows(float x[8], int g)
+{
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            if (!(j & h)) {
+                const float a = x[j], b = x[j + h];
+                x[j] = a + b;
+                x[j + h] = a - b;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        const bool upper = (g & m) != 0;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const float o = __shfl_xor(x[j], m);
+            x[j] = upper ? (o - x[j]) : (x[j] + o);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) x[j] = x[j] * kInvSqrt128;
+}
+
+// Smallest fp16 >= v (v > 0 finite), saturating at 65504.
+__device__ __forceinline__ uint32_t f16_ceil_bits(float v)
+{
+    if (v > 65504.0f) return 0x7bffu;
+    uint32_t h = f2h_bits(v);
+    if (h2f(h) < v) h += 1u;
+    return h;
+}
+
+// Nearest E8 point of u (8 floats); returns the codes c = 2y as bytes c + 64 in two dwords.
+// E8 = D8 u (D8 + 1/2) (Conway & Sloane). With f = rint(u), e = u - f, a = |e|:
+//   coset D8:       squared distance sum(a^2), plus (1 - 2 max a) if sum(f) is odd, where the
+//                   coordinate of largest a is re-rounded the other way;
+//   coset D8 + 1/2: nearest half-integers f + sign(e)/2 at distance (1/2 - a) each, sum
+//                   (2 - sum(a) + sum(a^2)), plus 2 min a if sum(f) - #(e < 0) is odd, where
+//                   the coordinate of smallest a moves to the other neighbouring half-integer.
+// The nearer coset wins (D8 on ties). Arg-max/min pack the index into the 3 low bits of |e|,
+// which can only matter between coordinates whose errors differ by a few ulps (a near-tie).
+__device__ __forceinline__ void e8_nearest_code(const float u[8], uint32_t &w0, uint32_t &w1)
+{
+    float f[8], e[8];
+    uint32_t kmax = 0u, kmin = 0xffffffffu, sx = 0u;
+    float sf = 0.0f, A2 = 0.0f, Sa = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        f[i] = __builtin_rintf(u[i]);
+        e[i] = u[i] - f[i];
+        const uint32_t ab = __float_as_uint(e[i]) & 0x7ffffff8u;
+        kmax = max(kmax, ab | (7u - (uint32_t)i));
+        kmin = min(kmin, ab | (uint32_t)i);
+        sx ^= __float_as_uint(e[i]);
+        sf += f[i];
+        A2 = __builtin_fmaf(e[i], e[i], A2);
+        Sa += __builtin_fabsf(e[i]);
+    }
+    const int P0 = ((int)sf) & 1;
+    const int P1 = P0 ^ (int)(sx >> 31);
+    const float amax = __uint_as_float(kmax & ~7u);
+    const float amin = __uint_as_float(kmin & ~7u);
+    const float d0 = P0 ? A2 + (1.0f - 2.0f * amax) : A2;
+    const float d1 = (2.0f - Sa + A2) + (P1 ? 2.0f * amin : 0.0f);
+    const bool half = d1 < d0;
+    const int jf = half ? (int)(kmin & 7u) : (int)(7u - (kmax & 7u));
+    const int par = half ? P1 : P0;
+    // e at index jf (select tree)
+    const float e01 = (jf & 1) ? e[1] : e[0];
+    const float e23 = (jf & 1) ? e[3] : e[2];
+    const float e45 = (jf & 1) ? e[5] : e[4];
+    const float e67 = (jf & 1) ? e[7] : e[6];
+    const float e03 = (jf & 2) ? e23 : e01;
+    const float e47 = (jf & 2) ? e67 : e45;
+    const float ej = (jf & 4) ? e47 : e03;
+    const float hs = half ? 1.0f : 0.0f;
+    uint32_t b0 = 0u, b1 = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        b0 = __builtin_amdgcn_cvt_pk_u8_f32(
+            __builtin_fmaf(2.0f, f[i], 64.0f + __builtin_copysignf(hs, e[i])), i, b0);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        b1 = __builtin_amdgcn_cvt_pk_u8_f32(
+            __builtin_fmaf(2.0f, f[i + 4], 64.0f + __builtin_copysignf(hs, e[i + 4])), i, b1);
+    if (par) {
+        // D8: re-round toward u (+2 sign(e)); D8 + 1/2: move away from u (-2 sign(e))
+        int d = (ej < 0.0f) ? -2 : 2;
+        if (half) d = -d;
+        const uint32_t add = (uint32_t)d << (8 * (jf & 3));
+        if (jf < 4) b0 += add; else b1 += add;
+    }
+    w0 = b0;
+    w1 = b1;
+}
+
+// Encodes one kept token of one chain for this lane's 8 dims. Returns the absolute code bytes
+// (offset +64) and the fp16 scale bits of this lane's group.
+template <bool IS_KEY>
+__device__ __forceinline__ uint2 encode_token(const CodecArgs &a, const uint16_t *__restrict__ X,
+                                              const int32_t *__restrict__ pos, int j, int g,
+                                              float rho, uint32_t &s16)
+{
+    int p = pos[j];
+    p = min(max(p, 0), a.T - 1);
+    float x[8];
+    load_f16x8(X + (size_t)p * kHeadDim, x);
+    if (IS_KEY) {
+        // RoPE removal, split-half pairs (i, i + 64) = lanes (g, g ^ 8):
+        // x_i = a*C + b*S, x_{i+64} = b*C - a*S with (a, b) = (k_i, k_{i+64}).
+        float c[8], s[8];
+        load_f32x8(a.rope_cos + (size_t)p * 64 + 8 * (g & 7), c);
+        load_f32x8(a.rope_sin + (size_t)p * 64 + 8 * (g & 7), s);
+        const bool upper = g >= 8;
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const float o = __shfl_xor(x[k], 8);
+            const float t1 = x[k] * c[k];
+            const float t2 = o * s[k];
+            x[k] = upper ? t1 - t2 : t1 + t2;
+        }
+    }
+    hadamard_rows(x, g);
+    float amax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) amax = fmaxf(amax, __builtin_fabsf(x[k]));
+    float u[8];
+    if (amax == 0.0f) {
+        s16 = 0u;
+#pragma unroll
+        for (int k = 0; k < 8; k++) u[k] = 0.0f;
+    } else {
+        s16 = f16_ceil_bits(amax / rho);
+        const float s = h2f(s16);
+#pragma unroll
+        for (int k = 0; k < 8; k++) u[k] = fminf(fmaxf(x[k] / s, -rho), rho);
+    }
+    uint2 c;
+    e8_nearest_code(u, c.x, c.y);
+    return c;
+}
+
+// Delta bytes (two's complement) from two offset-64 codes: per byte (a + 128) - b stays in
+// [96, 160] for codes within +-16, so no carry or borrow crosses a byte; xor 0x80 recentres.
+__device__ __forceinline__ uint2 delta_code(uint2 cur, uint2 prev)
+{
+    return make_uint2(((cur.x + 0x80808080u) - prev.x) ^ 0x80808080u,
+                      ((cur.y + 0x80808080u) - prev.y) ^ 0x80808080u);
+}
+
+template <bool IS_KEY>
+__device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile)
+{
+    __shared__ uint2 s_last[17][16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane & 15, q = wave * 4 + (lane >> 4);
+    const int n_keep = a.n_keep;
+    const size_t chain = (size_t)lc * a.H + h;
+    const uint16_t *X = (IS_KEY ? a.K : a.V) +
+                        ((size_t)(a.layer_begin + lc) * a.H + h) * (size_t)a.T * kHeadDim + 8 * g;
+    const int32_t *pos = a.positions + (size_t)lc * n_keep;
+    int8_t *codes = (IS_KEY ? a.codes_k : a.codes_v) + chain * (size_t)n_keep * kHeadDim + 8 * g;
+    uint16_t *scales = (IS_KEY ? a.scales_k : a.scales_v) + chain * (size_t)n_keep * kGroups + g;
+    const float rho = IS_KEY ? a.rho_k : a.rho_v;
+    const uint2 zero = make_uint2(0x40404040u, 0x40404040u);   // code 0 in offset form
+
+    // the tile's predecessor token, coded (not stored) by lane group 0
+    if (q == 0) {
+        uint2 hc = zero;
+        const int jh = tile * kCodecTile - 1;
+        if (jh >= 0) {
+            uint32_t s16;
+            hc = encode_token<IS_KEY>(a, X, pos, jh, g, rho, s16);
+        }
+        s_last[0][g] = hc;
+    }
+    const int j0 = tile * kCodecTile + q * kCodecRun;
+    uint2 first = zero, prev = zero;
+    for (int i = 0; i < kCodecRun; i++) {
+        const int j = j0 + i;
+        if (j < n_keep) {
+            uint32_t s16;
+            const uint2 c = encode_token<IS_KEY>(a, X, pos, j, g, rho, s16);
+            scales[(size_t)j * kGroups] = (uint16_t)s16;
+            if (i == 0)
+                first = c;
+            else
+                *reinterpret_cast<uint2 *>(codes + (size_t)j * kHeadDim) = delta_code(c, prev);
+            prev = c;
+        }
+    }
+    s_last[q + 1][g] = prev;
+    __syncthreads();
+    if (j0 < n_keep)
+        *reinterpret_cast<uint2 *>(codes + (size_t)j0 * kHeadDim) = delta_code(first, s_last[q][g]);
+}
+
+// grid: Lc * 2 * H * tiles_per_chain blocks, XCD-aware order (heads of one token tile adjacent)
+__global__ __launch_bounds__(kCodecThreads) void k_encode(CodecArgs a)
+{
+    const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
+    const int h = id % a.H;
+    uint32_t r = id / a.H;
+    const int tensor = r & 1;
+    r >>= 1;
+    const int tile = r % a.tiles_per_chain;
+    const int lc = r / a.tiles_per_chain;
+    if (tensor == 0)
+        encode_tile<true>(a, lc, h, tile);
+    else
+        encode_tile<false>(a, lc, h, tile);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Decode. Each tile needs the running sum of all earlier deltas of its chain; tiles publish
+// their own byte-wise sum and then their inclusive prefix (single-pass chained scan with
+// decoupled look-back). Tiles take tickets from an atomic counter in launch order, so every
+// tile a tile waits for has already started and makes progress.
+// ---------------------------------------------------------------------------------------------
+constexpr uint32_t kSpinLimit = 1u << 26;
+
+__global__ void k_decode_reset(uint32_t *flag, int n, uint32_t *ticket)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) flag[i] = 0u;
+    if (i < 2) ticket[i] = 0u;
+}
+
+template <bool IS_KEY>
+__device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off, int j, int g,
+                                             const int32_t *__restrict__ pos, uint2 code,
+                                             uint32_t s16)
+{
+    // code bytes are two's complement c; x = s * c / 2 (exact in fp32)
+    const float s = h2f(s16);
+    const float hs = 0.5f * s, off = -64.0f * s;
+    const uint32_t ub0 = code.x ^ 0x80808080u, ub1 = code.y ^ 0x80808080u;   // c + 128
+    float x[8];
+    x[0] = __builtin_fmaf(hs, (float)(ub0 & 0xffu), off);
+    x[1] = __builtin_fmaf(hs, (float)((ub0 >> 8) & 0xffu), off);
+    x[2] = __builtin_fmaf(hs, (float)((ub0 >> 16) & 0xffu), off);
+    x[3] = __builtin_fmaf(hs, (float)((ub0 >> 24) & 0xffu), off);
+    x[4] = __builtin_fmaf(hs, (float)(ub1 & 0xffu), off);
+    x[5] = __builtin_fmaf(hs, (float)((ub1 >> 8) & 0xffu), off);
+    x[6] = __builtin_fmaf(hs, (float)((ub1 >> 16) & 0xffu), off);
+    x[7] = __builtin_fmaf(hs, (float)((ub1 >> 24) & 0xffu), off);
+    hadamard_rows(x, g);
+    if (IS_KEY) {
+        // RoPE at the stored position: k_i = x_i*C - x_{i+64}*S, k_{i+64} = x_{i+64}*C + x_i*S
+        int p = pos[j];
+        p = min(max(p, 0), a.T - 1);
+        float c[8], sn[8];
+        load_f32x8(a.rope_cos + (size_t)p * 64 + 8 * (g & 7), c);
+        load_f32x8(a.rope_sin + (size_t)p * 64 + 8 * (g & 7), sn);
+        const bool upper = g >= 8;
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const float o = __shfl_xor(x[k], 8);
+            const float t1 = x[k] * c[k];
+            const float t2 = o * sn[k];
+            x[k] = upper ? t1 + t2 : t1 - t2;
+        }
+    }
+    const size_t o = row_off + (size_t)j * kHeadDim + 8 * g;
+    if (a.out_f32) {
+        float *dst = (float *)(IS_KEY ? a.out_k : a.out_v) + o;
+        *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4 *>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    } else {
+        uint16_t *dst = (uint16_t *)(IS_KEY ? a.out_k : a.out_v) + o;
+        uint4 v;
+        v.x = (uint32_t)f2h_bits(x[0]) | ((uint32_t)f2h_bits(x[1]) << 16);
+        v.y = (uint32_t)f2h_bits(x[2]) | ((uint32_t)f2h_bits(x[3]) << 16);
+        v.z = (uint32_t)f2h_bits(x[4]) | ((uint32_t)f2h_bits(x[5]) << 16);
+        v.w = (uint32_t)f2h_bits(x[6]) | ((uint32_t)f2h_bits(x[7]) << 16);
+        *reinterpret_cast<uint4 *>(dst) = v;
+    }
+}
+
+template <bool IS_KEY>
+__device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int ticket)
+{
+    __shared__ uint2 s_tot[16][16];
+    __shared__ uint2 s_excl[16];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane & 15, q = wave * 4 + (lane >> 4);
+    const int n_keep = a.n_keep;
+    const size_t chain = (size_t)lc * a.H + h;
+    const int8_t *codes = (IS_KEY ? a.codes_k : a.codes_v) + chain * (size_t)n_keep * kHeadDim + 8 * g;
+    const uint16_t *scales = (IS_KEY ? a.scales_k : a.scales_v) + chain * (size_t)n_keep * kGroups + g;
+    const int32_t *pos = a.positions + (size_t)lc * n_keep;
+    const int j0 = tile * kCodecTile + q * kCodecRun;
+
+    // 1. this lane group's deltas and their running sum
+    uint2 run[kCodecRun];
+    uint2 acc = make_uint2(0u, 0u);
+#pragma unroll
+    for (int i = 0; i < kCodecRun; i++) {
+        const int j = j0 + i;
+        uint2 d = make_uint2(0u, 0u);
+        if (j < n_keep) d = *reinterpret_cast<const uint2 *>(codes + (size_t)j * kHeadDim);
+        acc = make_uint2(add_bytes(acc.x, d.x), add_bytes(acc.y, d.y));
+        run[i] = acc;
+    }
+    s_tot[q][g] = acc;
+    __syncthreads();
+    // 2. prefix over the lane groups before this one, and the tile total (group 15's lanes)
+    uint2 gp = make_uint2(0u, 0u);
+    for (int k = 0; k < q; k++) {
+        const uint2 t = s_tot[k][g];
+        gp = make_uint2(add_bytes(gp.x, t.x), add_bytes(gp.y, t.y));
+    }
+    // 3. decoupled look-back, done by lane group 15 (it holds the tile total)
+    if (q == 15) {
+        const uint2 agg = make_uint2(add_bytes(gp.x, acc.x), add_bytes(gp.y, acc.y));
+        uint2 excl = make_uint2(0u, 0u);
+        if (tile == 0) {
+            a.lb_incl[(size_t)ticket * 16 + g] = agg;
+            __threadfence();
+            if (g == 0) __hip_atomic_store(&a.lb_flag[ticket], 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            a.lb_agg[(size_t)ticket * 16 + g] = agg;
+            __threadfence();
+            if (g == 0) __hip_atomic_store(&a.lb_flag[ticket], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            int pred = ticket - 1;
+            uint32_t spins = 0;
+            while (true) {
+                uint32_t f = __hip_atomic_load(&a.lb_flag[pred], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+                f = __builtin_amdgcn_readfirstlane(f);
+                if (f == 0u) {
+                    if (++spins > kSpinLimit) {   // never expected: report and give up
+                        if (g == 0) atomicOr(&a.lb_ticket[1], 1u);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                    continue;
+                }
+                const uint2 v = (f == 2u) ? a.lb_incl[(size_t)pred * 16 + g] : a.lb_agg[(size_t)pred * 16 + g];
+                excl = make_uint2(add_bytes(excl.x, v.x), add_bytes(excl.y, v.y));
+                if (f == 2u) break;
+                pred--;
+            }
+            const uint2 incl = make_uint2(add_bytes(excl.x, agg.x), add_bytes(excl.y, agg.y));
+            a.lb_incl[(size_t)ticket * 16 + g] = incl;
+            __threadfence();
+            if (g == 0) __hip_atomic_store(&a.lb_flag[ticket], 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        s_excl[g] = excl;
+    }
+    __syncthreads();
+    const uint2 base0 = s_excl[g];
+    const uint2 base = make_uint2(add_bytes(base0.x, gp.x), add_bytes(base0.y, gp.y));
+    // 4. reconstruct every token of this lane group
+    const size_t row_off = chain * (size_t)n_keep * kHeadDim;
+#pragma unroll
+    for (int i = 0; i < kCodecRun; i++) {
+        const int j = j0 + i;
+        if (j < n_keep) {
+            const uint2 c = make_uint2(add_bytes(base.x, run[i].x), add_bytes(base.y, run[i].y));
+            const uint32_t s16 = scales[(size_t)j * kGroups];
+            decode_store<IS_KEY>(a, row_off, j, g, pos, c, s16);
+        }
+    }
+}
+
+// grid: Lc * 2 * H * tiles_per_chain blocks; the logical tile comes from the ticket, ordered
+// chain-major so a tile's predecessors in its chain hold smaller tickets.
+__global__ __launch_bounds__(kCodecThreads) void k_decode(CodecArgs a)
+{
+    __shared__ int s_ticket;
+    if (threadIdx.x == 0) s_ticket = (int)atomicAdd(&a.lb_ticket[0], 1u);
+    __syncthreads();
+    const int ticket = s_ticket;
+    const int tile = ticket % a.tiles_per_chain;
+    uint32_t r = ticket / a.tiles_per_chain;
+    const int h = r % a.H;
+    r /= a.H;
+    const int tensor = r & 1;
+    const int lc = r >> 1;
+    if (tensor == 0)
+        decode_tile<true>(a, lc, h, tile, ticket);
+    else
+        decode_tile<false>(a, lc, h, tile, ticket);
+}
+
+}  // namespace nq

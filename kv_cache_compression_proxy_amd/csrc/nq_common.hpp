@@ -1,0 +1,70 @@
+// Device helpers shared by the gfx950 kernels of libnq.
+//
+// Lane layout used by every row kernel: a 128-float head row is spread over 16 consecutive
+// lanes, lane g (= lane & 15) holding the 8 consecutive dims [8g, 8g+8) -- one 16-byte fp16
+// load per lane, a fully coalesced 256-byte row per lane group, and one E8 group per lane.
+// A wave64 therefore works on 4 rows at once ("lane groups" 0..3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nq {
+
+constexpr int kHeadDim = 128;
+constexpr int kGroups = 16;                       // 8-float groups per row
+constexpr float kInvSqrt128 = 0x1.6a09e6p-4f;    // fp32 nearest to 1/sqrt(128)
+
+__device__ __forceinline__ float h2f(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ __forceinline__ uint16_t f2h_bits(float x)   // round to nearest even
+{
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// 8 fp16 values (one 16-byte load) -> fp32
+__device__ __forceinline__ void load_f16x8(const uint16_t *__restrict__ p, float x[8])
+{
+    const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        x[2 * k] = h2f(w[k] & 0xffffu);
+        x[2 * k + 1] = h2f(w[k] >> 16);
+    }
+}
+
+__device__ __forceinline__ void load_f32x8(const float *__restrict__ p, float x[8])
+{
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// Byte-wise (mod 256) addition of four packed bytes, no carries between bytes.
+__device__ __forceinline__ uint32_t add_bytes(uint32_t a, uint32_t b)
+{
+    return ((a & 0x7f7f7f7fu) + (b & 0x7f7f7f7fu)) ^ ((a ^ b) & 0x80808080u);
+}
+
+// Byte-wise (mod 256) subtraction a - b.
+__device__ __forceinline__ uint32_t sub_bytes(uint32_t a, uint32_t b)
+{
+    return ((a | 0x80808080u) - (b & 0x7f7f7f7fu)) ^ ((a ^ ~b) & 0x80808080u);
+}
+
+// Workgroup-to-XCD aware block order. The dispatcher hands consecutive workgroup ids to the 8
+// XCDs round robin; this maps the hardware id to a logical id so that logically consecutive
+// blocks (which share cached rows, e.g. the rotary table of one token tile) run on one XCD and
+// share its L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t n)
+{
+    const uint32_t per = n >> 3, rem = n & 7u, x = b & 7u;
+    return x * per + (x < rem ? x : rem) + (b >> 3);
+}
+
+}  // namespace nq

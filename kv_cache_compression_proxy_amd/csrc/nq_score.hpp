@@ -1,0 +1,232 @@
+// Key-key proxy scoring and eviction (steps 1-2).
+//
+// "NexusQuant：无需训练实现LLM KV缓存10-33倍压缩的技术突破", sections "Token淘汰机制" (drop the
+// least important tokens, always keep BOS and a recent sliding window) and "技术实现细节"
+// (key-key proxy scorer, no extra computation); "Como comprimir o KV cache do seu LLM em 33x sem
+// treino", "Como funciona" steps 1-2 (cross-head inner product).
+//
+// The recent window's keys stand in for queries: qbar_h = sum of the last W keys of head h
+// (fp64: exact for fp16 inputs), and a candidate's score is s_t = sum_h <qbar_h, k_{h,t}>
+// (fp64). The scorer is a GEMV over all of K -- HBM bound, no matrix cores.
+#pragma once
+
+#include "nq_common.hpp"
+
+namespace nq {
+
+// ---- window sums: one block per (compressed layer, head) ----------------------------------
+__global__ __launch_bounds__(256) void k_window_sum(const uint16_t *__restrict__ K, int H, int T,
+                                                   int W, int layer_begin,
+                                                   double *__restrict__ qbar)
+{
+    __shared__ double red[16][kHeadDim];
+    const int lh = blockIdx.x;
+    const int lc = lh / H, h = lh % H;
+    const int g = threadIdx.x & 15, slot = threadIdx.x >> 4;
+    const uint16_t *base = K + ((size_t)(layer_begin + lc) * H + h) * (size_t)T * kHeadDim + 8 * g;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int w = max(0, T - W) + slot; w < T; w += 16) {
+        float x[8];
+        load_f16x8(base + (size_t)w * kHeadDim, x);
+#pragma unroll
+        for (int k = 0; k < 8; k++) acc[k] += (double)x[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) red[slot][8 * g + k] = acc[k];
+    __syncthreads();
+    if (threadIdx.x < kHeadDim) {
+        double s = 0.0;
+        for (int r = 0; r < 16; r++) s += red[r][threadIdx.x];   // exact: fp16 sums fit fp64
+        qbar[(size_t)lh * kHeadDim + threadIdx.x] = s;
+    }
+}
+
+// ---- scores: block = 64 tokens of one compressed layer; lane group per row -----------------
+constexpr int kScoreTile = 64;
+
+__global__ __launch_bounds__(256) void k_scores(const uint16_t *__restrict__ K,
+                                                const double *__restrict__ qbar, int H, int T,
+                                                int W, int layer_begin, int tiles,
+                                                double *__restrict__ scores)
+{
+    const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
+    const int lc = id / tiles, tile = id % tiles;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane & 15, r4 = lane >> 4;
+    const int c_end = T - W;                        // candidates: [1, c_end)
+    const uint16_t *Kl = K + (size_t)(layer_begin + lc) * H * (size_t)T * kHeadDim + 8 * g;
+    const double *qb = qbar + (size_t)lc * H * kHeadDim + 8 * g;
+    int t[4];
+    bool ok[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        t[u] = tile * kScoreTile + wave * 16 + u * 4 + r4;
+        ok[u] = t[u] >= 1 && t[u] < c_end;
+    }
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int h = 0; h < H; h++) {
+        double q[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) q[k] = qb[(size_t)h * kHeadDim + k];
+        const uint16_t *Kh = Kl + (size_t)h * T * kHeadDim;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            if (ok[u]) {
+                float x[8];
+                load_f16x8(Kh + (size_t)t[u] * kHeadDim, x);
+#pragma unroll
+                for (int k = 0; k < 8; k++) acc[u] = __builtin_fma(q[k], (double)x[k], acc[u]);
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) acc[u] += __shfl_xor(acc[u], m);
+        if (g == 0 && ok[u]) scores[(size_t)lc * T + t[u]] = acc[u];
+    }
+}
+
+// ---- selection: one 1024-thread block per compressed layer ---------------------------------
+// Keeps the m best candidates by (score desc, position asc): an MSB-first radix select over
+// order-preserving 64-bit keys finds the m-th best key exactly, then one ordered pass emits BOS,
+// the window, the candidates above that key and the lowest-positioned ones equal to it.
+constexpr int kSelThreads = 1024;
+
+__device__ __forceinline__ uint64_t order_key(double d)
+{
+    uint64_t b = (uint64_t)__double_as_longlong(d);
+    if (d == 0.0) b = 0ull;                               // -0 and +0 are one key
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// exclusive block scan of one uint32 per thread (1024 threads = 16 waves)
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *s_wave, uint32_t &total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+    for (int w = 0; w < kSelThreads / 64; w++) {
+        const uint32_t x = s_wave[w];
+        if (w < wave) before += x;
+        all += x;
+    }
+    __syncthreads();
+    total = all;
+    return before + incl - v;
+}
+
+__global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict__ scores, int T,
+                                                        int W, int n_keep,
+                                                        int32_t *__restrict__ positions)
+{
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t s_wave[kSelThreads / 64];
+    __shared__ uint64_t s_prefix, s_mask;
+    __shared__ int s_krem, s_all;
+    const int lc = blockIdx.x;
+    const double *s = scores + (size_t)lc * T;
+    int32_t *out = positions + (size_t)lc * n_keep;
+    const int tid = threadIdx.x;
+    const int c_end = T - W;
+    const int n_cand = c_end > 1 ? c_end - 1 : 0;
+    const int m = n_keep - (T - n_cand);
+    const bool partial = m > 0 && m < n_cand;
+
+    if (tid == 0) { s_prefix = 0ull; s_mask = 0ull; s_krem = m; s_all = 0; }
+    __syncthreads();
+    if (partial) {
+        for (int pass = 0; pass < 8; pass++) {
+            const int shift = 56 - 8 * pass;
+            if (tid < 256) hist[tid] = 0u;
+            __syncthreads();
+            const uint64_t prefix = s_prefix, mask = s_mask;
+            for (int t = 1 + tid; t < c_end; t += kSelThreads) {
+                const uint64_t k = order_key(s[t]);
+                if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid < 64) {
+                // lane L covers digits 255-4L .. 252-4L (descending); find the digit holding
+                // the krem-th largest key
+                const int krem = s_krem;
+                uint32_t c[4], loc = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) { c[i] = hist[255 - 4 * tid - i]; loc += c[i]; }
+                uint32_t incl = loc;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const uint32_t o = __shfl_up(incl, d);
+                    if (tid >= d) incl += o;
+                }
+                uint32_t above = incl - loc;               // keys in higher digits
+                if (above < (uint32_t)krem && incl >= (uint32_t)krem) {
+                    for (int i = 0; i < 4; i++) {
+                        if (above + c[i] >= (uint32_t)krem) {
+                            const uint32_t dgt = 255 - 4 * tid - i;
+                            s_prefix = prefix | ((uint64_t)dgt << shift);
+                            s_mask = mask | (255ull << shift);
+                            s_krem = krem - (int)above;
+                            if (c[i] == (uint32_t)(krem - (int)above)) s_all = 1;
+                            break;
+                        }
+                        above += c[i];
+                    }
+                }
+            }
+            __syncthreads();
+            if (s_all) break;                              // the whole bucket is kept
+        }
+    }
+    const uint64_t prefix = s_prefix, mask = s_mask;
+    const int krem = s_krem;
+    const bool take_all_eq = s_all != 0;
+    // ordered emission: chunks of 4 consecutive positions per thread
+    uint32_t eq_base = 0, out_base = 0;
+    for (int t0 = 0; t0 < T; t0 += 4 * kSelThreads) {
+        const int tb = t0 + 4 * tid;
+        uint32_t keepf = 0, eqf = 0;
+        uint32_t gt4 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int t = tb + i;
+            if (t >= T) continue;
+            const bool cand = t >= 1 && t < c_end;
+            if (!cand) { keepf |= 1u << i; continue; }
+            if (!partial) { if (m > 0) keepf |= 1u << i; continue; }
+            const uint64_t k = order_key(s[t]) & mask;
+            if (k > prefix) gt4 |= 1u << i;
+            else if (k == prefix) eqf |= 1u << i;
+        }
+        uint32_t eq_tot;
+        const uint32_t eq_before = block_excl_scan(__builtin_popcount(eqf), s_wave, eq_tot);
+        uint32_t r = eq_base + eq_before;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            if (gt4 & (1u << i)) keepf |= 1u << i;
+            if (eqf & (1u << i)) {
+                if (take_all_eq || r < (uint32_t)krem) keepf |= 1u << i;
+                r++;
+            }
+        }
+        eq_base += eq_tot;
+        uint32_t k_tot;
+        uint32_t o = out_base + block_excl_scan(__builtin_popcount(keepf), s_wave, k_tot);
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            if (keepf & (1u << i)) {
+                if (o < (uint32_t)n_keep) out[o] = tb + i;   // never past the caller's row
+                o++;
+            }
+        out_base += k_tot;
+    }
+}
+
+}  // namespace nq

@@ -1,0 +1,154 @@
+"""Shared helpers of the GPU parity tests: upload seeded inputs, run the HIP path through the C
+ABI, run the oracle on the same host bytes, and compare with the parity rules (keep-sets and
+codes bit-exact except counted near-ties; reconstructions within tolerance)."""
+from __future__ import annotations
+
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+import kv_cache_compression_proxy_amd as nq
+import kvsynth
+import oracle
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def params_of(w: kvsynth.Workload, tokens=None) -> nq.NqParams:
+    return nq.make_params(w.layers, w.kv_heads, w.tokens if tokens is None else tokens, w.window,
+                          w.evict_permille, w.bits_k, w.bits_v, w.rope_base, w.layer_begin,
+                          w.layer_end)
+
+
+def upload(w: kvsynth.Workload, tokens=None, chunk=8, only_layers=None):
+    """Device K, V [L, H, T, 128] fp16, generated on the host chunk by chunk."""
+    T = w.tokens if tokens is None else tokens
+    K = torch.empty((w.layers, w.kv_heads, T, 128), dtype=torch.float16, device="cuda")
+    V = torch.empty_like(K)
+    layers = list(range(w.layers)) if only_layers is None else list(only_layers)
+    for i in range(0, len(layers), chunk):
+        ls = layers[i:i + chunk]
+        hk = np.empty((len(ls), w.kv_heads, T, 128), np.float16)
+        hv = np.empty_like(hk)
+
+        def one(k):
+            hk[k], hv[k] = kvsynth.layer_kv(w, ls[k], T)
+        with ThreadPoolExecutor(8) as ex:
+            list(ex.map(one, range(len(ls))))
+        for k, l in enumerate(ls):
+            K[l].copy_(torch.from_numpy(hk[k]))
+            V[l].copy_(torch.from_numpy(hv[k]))
+    torch.cuda.synchronize()
+    return K, V
+
+
+class GpuRun:
+    """Whole hot path on the GPU for parameters p and device K, V."""
+
+    def __init__(self, p: nq.NqParams, K, V, positions=None, decode=True, out_f32=True):
+        self.p = p
+        self.K, self.V, self.out_f32 = K, V, out_f32
+        Lc = p.layer_end - p.layer_begin
+        n = nq.nq_keep_count(p)
+        self.n_keep = n
+        dev = K.device
+        self.cos, self.sin = nq.rope_table(p, dev)
+        T = p.tokens
+        self.scores = torch.full((max(Lc, 1), max(T, 1)), float("nan"), dtype=torch.float64,
+                                 device=dev)
+        if positions is None:
+            self.positions = torch.empty((max(Lc, 1), max(n, 1)), dtype=torch.int32, device=dev)
+            ws = nq.workspace(nq.nq_score_evict_workspace_bytes(p), dev)
+            nq.nq_score_evict(p, K, self.positions, ws, scores=self.scores)
+        else:
+            self.positions = positions.to(dev).contiguous()
+        H = p.kv_heads
+        self.codes_k = torch.empty((max(Lc, 1), H, max(n, 1), 128), dtype=torch.int8, device=dev)
+        self.codes_v = torch.empty_like(self.codes_k)
+        self.scales_k = torch.empty((max(Lc, 1), H, max(n, 1), 16), dtype=torch.float16,
+                                    device=dev)
+        self.scales_v = torch.empty_like(self.scales_k)
+        nq.nq_encode(p, K, V, self.positions, self.cos, self.sin, self.codes_k, self.codes_v,
+                     self.scales_k, self.scales_v)
+        if decode:
+            dt = torch.float32 if out_f32 else torch.float16
+            self.K_hat = torch.empty((max(Lc, 1), H, max(n, 1), 128), dtype=dt, device=dev)
+            self.V_hat = torch.empty_like(self.K_hat)
+            self.dws = nq.workspace(nq.nq_decode_workspace_bytes(p), dev)
+            nq.nq_decode(p, self.codes_k, self.codes_v, self.scales_k, self.scales_v,
+                         self.positions, self.cos, self.sin, self.K_hat, self.V_hat,
+                         nq.NQ_OUT_F32 if out_f32 else nq.NQ_OUT_F16, self.dws)
+        torch.cuda.synchronize()
+
+    def lookback_error(self) -> int:
+        """Spin-limit flag of the decode's tile look-back (0 when every wait ended normally)."""
+        ws = self.dws.cpu().numpy().view(np.uint32)
+        Lc = self.p.layer_end - self.p.layer_begin
+        tiles = Lc * 2 * self.p.kv_heads * ((self.n_keep + 255) // 256)
+        off = ((tiles + 1) * 4 + 255) // 256 * 256 // 4
+        return int(ws[off + 1])
+
+
+def absolute_codes(d: np.ndarray) -> np.ndarray:
+    """Running sum mod 256 of delta codes along axis -2 (tokens) -> int8 absolute codes."""
+    c = np.cumsum(d.astype(np.int64), axis=-2)
+    return (((c + 128) % 256) - 128).astype(np.int8)
+
+
+def compare_keep(gpu_pos: np.ndarray, ora_pos: np.ndarray, near: np.ndarray):
+    """-> (number of differing positions, all differences are eviction near-ties)."""
+    a, b = set(gpu_pos.tolist()), set(ora_pos.tolist())
+    diff = a ^ b
+    return len(diff), all(near[t] for t in diff)
+
+
+def compare_codes(gc_abs, gs, oc_abs, os_, flags):
+    """Group-level comparison; -> (mismatching groups, mismatches that are not near-ties,
+    flagged groups)."""
+    gcode = gc_abs.reshape(gc_abs.shape[:-1] + (16, 8))
+    ocode = oc_abs.reshape(oc_abs.shape[:-1] + (16, 8))
+    mism = np.any(gcode != ocode, axis=-1) | (gs.view(np.uint16) != os_.view(np.uint16))
+    bad = mism & (flags == 0)
+    return int(mism.sum()), int(bad.sum()), int((flags != 0).sum())
+
+
+def recon_ratio(gpu_hat, ora_hat, scales, flags):
+    """max over token-heads without flagged groups of max|gpu - oracle| / max group scale."""
+    s = scales.view(np.float16).astype(np.float64).max(axis=-1)
+    ok = ~np.any(flags != 0, axis=-1)
+    err = np.abs(gpu_hat.astype(np.float64) - ora_hat).max(axis=-1)
+    r = np.where(ok & (s > 0), err / np.where(s > 0, s, 1), 0.0)
+    zero_rows = ok & (s == 0)
+    return float(r.max(initial=0.0)), float(err[zero_rows].max(initial=0.0))
+
+
+def fp16_recon_ratio(gpu16: np.ndarray, ora64: np.ndarray, scales, flags) -> float:
+    """Like recon_ratio for fp16 outputs: the error left after taking away half a binary16 ulp
+    of the output (its final rounding), relative to the token-head's largest group scale."""
+    g = gpu16.astype(np.float64)
+    mag = np.maximum(np.abs(g), 2.0 ** -14)
+    half_ulp = 2.0 ** (np.floor(np.log2(mag)) - 11)
+    excess = np.maximum(np.abs(g - ora64) - half_ulp, 0.0).max(axis=-1)
+    s = scales.view(np.float16).astype(np.float64).max(axis=-1)
+    ok = ~np.any(flags != 0, axis=-1)
+    r = np.where(ok, excess / np.where(s > 0, s, 1.0), 0.0)
+    return float(r.max(initial=0.0))
+
+
+def fp16_ulps(gpu16: np.ndarray, ora64: np.ndarray, flags=None) -> int:
+    """max distance in binary16 ulps between the GPU fp16 output and the oracle's value rounded
+    to binary16 (numpy rounds to nearest even), over token-heads without near-tie groups."""
+    a = gpu16.view(np.uint16).astype(np.int32)
+    b = ora64.astype(np.float16).view(np.uint16).astype(np.int32)
+    # map sign-magnitude bit patterns to a monotone integer line
+    a = np.where(a & 0x8000, -(a & 0x7fff), a)
+    b = np.where(b & 0x8000, -(b & 0x7fff), b)
+    d = np.abs(a - b).max(axis=-1)
+    if flags is not None:
+        d = np.where(np.any(flags != 0, axis=-1), 0, d)
+    return int(d.max(initial=0))

@@ -1,0 +1,126 @@
+"""The C ABI without a GPU: libnq.so loads, exports every function include/nq.h declares, and
+its host-side logic (keep count, parameter checks, workspace sizing, error paths that return
+before any launch) behaves as documented."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import kv_cache_compression_proxy_amd as nq
+import kvsynth
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "nq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    lib = C.CDLL(nq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(nq.EXPORTED)
+
+
+def params(w, **kw):
+    d = dict(layers=w.layers, kv_heads=w.kv_heads, tokens=w.tokens, window=w.window,
+             evict_permille=w.evict_permille, bits_k=w.bits_k, bits_v=w.bits_v,
+             rope_base=w.rope_base, layer_begin=w.layer_begin, layer_end=w.layer_end)
+    d.update(kw)
+    return nq.make_params(**d)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3])
+def test_keep_count_matches_oracle(idx):
+    w = kvsynth.workload(idx)
+    p = params(w)
+    assert nq.nq_check_params(p) == nq.NQ_OK
+    assert nq.nq_keep_count(p) == oracle.keep_count(w.tokens, w.window, w.evict_permille)
+
+
+def test_keep_count_values_for_workloads():
+    assert [nq.nq_keep_count(params(kvsynth.workload(i))) for i in range(4)] == \
+        [820, 13108, 26215, 42599]
+
+
+@pytest.mark.parametrize("T,W,e", [(0, 0, 600), (1, 0, 600), (5, 10, 600), (1000, 0, 1000),
+                                   (1000, 999, 600), (7, 2, 0), (123457, 513, 777)])
+def test_keep_count_edges(T, W, e):
+    p = nq.make_params(1, 2, T, W, e, 3, 2, 1e4)
+    assert nq.nq_keep_count(p) == oracle.keep_count(T, W, e)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, nq.NQ_ERR_UNSUPPORTED), ("bits_k", 5, nq.NQ_ERR_UNSUPPORTED),
+    ("bits_v", 1, nq.NQ_ERR_INVALID_ARG), ("layers", 0, nq.NQ_ERR_INVALID_ARG),
+    ("kv_heads", 0, nq.NQ_ERR_INVALID_ARG), ("tokens", -1, nq.NQ_ERR_INVALID_ARG),
+    ("window", -1, nq.NQ_ERR_INVALID_ARG), ("evict_permille", 1001, nq.NQ_ERR_INVALID_ARG),
+    ("layer_end", 2, nq.NQ_ERR_INVALID_ARG), ("layer_begin", 1, nq.NQ_ERR_INVALID_ARG),
+    ("rope_base", 1.0, nq.NQ_ERR_INVALID_ARG), ("rope_base", float("nan"), nq.NQ_ERR_INVALID_ARG),
+])
+def test_invalid_params_rejected(field, value, status):
+    p = params(kvsynth.workload(0))
+    setattr(p, field, value)
+    if field == "layer_begin":
+        p.layer_end = 0   # begin > end
+    assert nq.nq_check_params(p) == status
+    assert nq.nq_keep_count(p) == -1
+    assert nq.nq_score_evict_workspace_bytes(p) == 0
+    fake = 1 << 20   # never dereferenced: validation fails before any launch
+    with pytest.raises(nq.NqError) as ei:
+        nq.nq_score_evict(p, fake, fake, None, stream=0)
+    assert ei.value.status == status
+    with pytest.raises(nq.NqError):
+        nq.nq_encode(p, fake, fake, fake, fake, fake, fake, fake, fake, fake, stream=0)
+
+
+def test_pointer_and_workspace_errors_before_launch():
+    p = params(kvsynth.workload(0))
+    fake = 1 << 20
+    with pytest.raises(nq.NqError) as ei:                       # null K
+        nq.nq_score_evict(p, None, fake, None, stream=0)
+    assert ei.value.status == nq.NQ_ERR_INVALID_ARG
+    with pytest.raises(nq.NqError) as ei:                       # misaligned K
+        nq.nq_encode(p, fake + 2, fake, fake, fake, fake, fake, fake, fake, fake, stream=0)
+    assert ei.value.status == nq.NQ_ERR_INVALID_ARG
+    lib = C.CDLL(nq.LIB_PATH)
+    f = lib.nq_score_evict
+    f.argtypes = [C.POINTER(nq.NqParams)] + [C.c_void_p] * 4 + [C.c_size_t, C.c_void_p]
+    need = nq.nq_score_evict_workspace_bytes(p)
+    assert need > 0
+    assert f(C.byref(p), fake, fake, None, fake, need - 1, None) == nq.NQ_ERR_WORKSPACE
+    assert f(C.byref(p), fake, fake, None, None, need, None) == nq.NQ_ERR_WORKSPACE
+    g = lib.nq_decode
+    g.argtypes = [C.POINTER(nq.NqParams)] + [C.c_void_p] * 9 + [C.c_int, C.c_void_p, C.c_size_t,
+                                                                  C.c_void_p]
+    dn = nq.nq_decode_workspace_bytes(p)
+    assert g(C.byref(p), *([fake] * 9), 0, fake, dn - 1, None) == nq.NQ_ERR_WORKSPACE
+    assert g(C.byref(p), *([fake] * 9), 7, fake, dn, None) == nq.NQ_ERR_INVALID_ARG
+    assert nq.nq_attend_workspace_bytes(p, 12, 100) == 0                  # 12 % 8 != 0
+    with pytest.raises(nq.NqError) as ei:                       # G = 16 unsupported
+        nq.nq_attend_decode(p, fake, 128, fake, fake, 10, fake, None, stream=0)
+    assert ei.value.status == nq.NQ_ERR_UNSUPPORTED
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert nq.nq_status_string(s) != "unknown status"
+    assert nq.nq_status_string(-99) == "unknown status"
+
+
+def test_presets():
+    p = nq.params_for("high", 28, 4, 65536, rope_base=1e6)
+    assert (p.layer_begin, p.layer_end, p.evict_permille, p.bits_k, p.bits_v) == (2, 26, 350, 3, 2)
+    w = kvsynth.workload(1)
+    q = nq.params_for("balanced", w.layers, w.kv_heads, w.tokens)
+    assert (q.window, q.evict_permille, q.bits_k, q.bits_v) == (w.window, w.evict_permille,
+                                                                w.bits_k, w.bits_v)
+    with pytest.raises(ValueError):
+        nq.params_for("asym", 1, 1, 1)
