@@ -1,0 +1,236 @@
+"""Benchmark of the KV-cache compression hot path on one MI355X.
+
+One step = the whole path over one synthetic prefill cache resident in HBM: nq_score_evict
+(window sums, proxy scores, eviction), nq_encode (RoPE removal, Hadamard, E8, delta) and
+nq_decode (running sum, dequantisation, inverse Hadamard, RoPE, fp16 store). The default
+workload is the Mistral-7B-shaped balanced preset: 32 layers x 8 kv heads x 32768 tokens x 128,
+fp16, K3V2, 60% eviction, BOS + 256-token window.
+
+Prints ONE JSON line on stdout (diagnostics go to stderr):
+  value      fp16-KV GB/s of the step = (fp16 K+V bytes encoded + fp16 K+V bytes decoded) /
+             (time of the step); encode and decode rates are reported separately too
+  roofline   for the dominant kernel (the one with the largest share of the step): algorithmic
+             HBM bytes per launch / its average launch time (HIP events on the launch stream),
+             against MI355X's 8 TB/s
+  cpu_baseline  the CPU oracle timed on a bounded sample (a few layers) of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3])
+    ap.add_argument("--cpu-layers", type=int, default=4,
+                    help="layers of the workload the CPU oracle baseline processes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                      "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, n_keep):
+    """Bytes the method must move per launch of each kernel group (no cache reuse assumed)."""
+    Lc, H, T = w.compressed_layers, w.kv_heads, w.tokens
+    row = 256                                            # one fp16 head row
+    kept_th = Lc * H * n_keep                            # kept token-heads
+    enc = kept_th * (2 * row + 2 * 128 + 2 * 32)         # K+V rows in, codes + scales out
+    enc += Lc * n_keep * 4 + T * 64 * 4 * 2              # positions; rotary table once
+    dec = kept_th * (2 * 128 + 2 * 32 + 2 * row)         # codes + scales in, fp16 K+V out
+    dec += Lc * n_keep * 4 + T * 64 * 4 * 2
+    n_cand = max(T - w.window - 1, 0)
+    score = Lc * H * T * row                             # one pass over all keys
+    score += Lc * T * 8 * 2 + Lc * n_keep * 4            # scores written + read, positions
+    return {"score_evict": score, "encode": enc, "decode": dec}
+
+
+def cpu_baseline(w, layers: int):
+    import kvsynth
+    import oracle
+    T = w.tokens
+    Ct, St = oracle.rope_table(T, w.rope_base)
+    t_enc = t_dec = 0.0
+    for l in range(layers):
+        K, V = kvsynth.layer_kv(w, w.layer_begin + l)
+        t0 = time.perf_counter()
+        enc = oracle.compress_layer(K, V, w.window, w.evict_permille, w.bits_k, w.bits_v, Ct, St)
+        t1 = time.perf_counter()
+        oracle.decode_layer(enc["codes_k"], enc["codes_v"], enc["scales_k"], enc["scales_v"],
+                            enc["positions"], Ct, St)
+        t2 = time.perf_counter()
+        t_enc += t1 - t0
+        t_dec += t2 - t1
+        log(f"[cpu] layer {l}: encode {t1 - t0:.2f}s decode {t2 - t1:.2f}s")
+    n_keep = oracle.keep_count(T, w.window, w.evict_permille)
+    kv_enc = layers * w.kv_heads * T * 256 * 2
+    kv_dec = layers * w.kv_heads * n_keep * 256 * 2
+    return {
+        "value": round((kv_enc + kv_dec) / (t_enc + t_dec) / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{layers} of {w.compressed_layers} layers of the same workload (score, evict, "
+                  f"encode, decode per layer; single-threaded C oracle, inputs in host RAM, "
+                  f"generation excluded)",
+        "encode_GBps": round(kv_enc / t_enc / 1e9, 4),
+        "decode_GBps": round(kv_dec / t_dec / 1e9, 4),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}). The hot path shards by layer with no communication; run "
+              f"with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import kv_cache_compression_proxy_amd as nq
+    import kvsynth
+
+    w = kvsynth.workload(args.workload)
+    p = nq.make_params(w.layers, w.kv_heads, w.tokens, w.window, w.evict_permille, w.bits_k,
+                       w.bits_v, w.rope_base, w.layer_begin, w.layer_end)
+    Lc, H, T = w.compressed_layers, w.kv_heads, w.tokens
+    n_keep = nq.nq_keep_count(p)
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: Lc={Lc} H={H} T={T} n_keep={n_keep}")
+
+    t0 = time.time()
+    K = torch.empty((w.layers, H, T, 128), dtype=torch.float16, device=dev)
+    V = torch.empty_like(K)
+    chunk = 4
+    for l0 in range(0, w.layers, chunk):
+        ls = list(range(l0, min(w.layers, l0 + chunk)))
+        hk = np.empty((len(ls), H, T, 128), np.float16)
+        hv = np.empty_like(hk)
+
+        def one(i):
+            hk[i], hv[i] = kvsynth.layer_kv(w, ls[i])
+        with ThreadPoolExecutor(8) as ex:
+            list(ex.map(one, range(len(ls))))
+        K[l0:l0 + len(ls)].copy_(torch.from_numpy(hk))
+        V[l0:l0 + len(ls)].copy_(torch.from_numpy(hv))
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated and uploaded in {time.time() - t0:.1f}s")
+
+    cos, sin = nq.rope_table(p, dev)
+    positions = torch.empty((Lc, n_keep), dtype=torch.int32, device=dev)
+    ws_s = nq.workspace(nq.nq_score_evict_workspace_bytes(p), dev)
+    ck = torch.empty((Lc, H, n_keep, 128), dtype=torch.int8, device=dev)
+    cv = torch.empty_like(ck)
+    sk = torch.empty((Lc, H, n_keep, 16), dtype=torch.float16, device=dev)
+    sv = torch.empty_like(sk)
+    Ko = torch.empty((Lc, H, n_keep, 128), dtype=torch.float16, device=dev)
+    Vo = torch.empty_like(Ko)
+    ws_d = nq.workspace(nq.nq_decode_workspace_bytes(p), dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        nq.nq_score_evict(p, K, positions, ws_s, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        nq.nq_encode(p, K, V, positions, cos, sin, ck, cv, sk, sv, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        nq.nq_decode(p, ck, cv, sk, sv, positions, cos, sin, Ko, Vo, nq.NQ_OUT_F16, ws_d, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / args.steps
+    phase = {"score_evict": 0.0, "encode": 0.0, "decode": 0.0}
+    for e in evs:
+        phase["score_evict"] += e[0].elapsed_time(e[1])
+        phase["encode"] += e[1].elapsed_time(e[2])
+        phase["decode"] += e[2].elapsed_time(e[3])
+    phase = {k: v / args.steps for k, v in phase.items()}
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}); "
+        f"phases ms: " + ", ".join(f"{k} {v:.3f}" for k, v in phase.items()))
+
+    kv_enc = Lc * H * T * 256 * 2
+    kv_dec = Lc * H * n_keep * 256 * 2
+    value = (kv_enc + kv_dec) / (ms_step * 1e-3) / 1e9
+    alg = algorithmic_bytes(w, n_keep)
+    dom = max(phase, key=phase.get)
+    kernel_of = {"score_evict": "k_window_sum+k_scores+k_select", "encode": "k_encode",
+                 "decode": "k_decode_reset+k_decode"}
+    achieved = alg[dom] / (phase[dom] * 1e-3) / 1e9
+    traffic = None
+    try:
+        tr = json.load(open(args.traffic))
+        ent = tr.get(w.name, {}).get(dom)
+        if ent:
+            traffic = ent["bytes_per_launch"]
+    except (OSError, ValueError):
+        pass
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": kernel_of[dom], "algorithmic_bytes_per_launch": alg[dom],
+                "avg_launch_ms": round(phase[dom], 4)}
+    out = {
+        "metric": "encode/decode fp16-KV GB/s on 1 MI355X; % of HBM peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "kv_heads": H, "tokens": T,
+                   "head_dim": 128, "window": w.window, "evict_permille": w.evict_permille,
+                   "bits_k": w.bits_k, "bits_v": w.bits_v, "rope_base": w.rope_base,
+                   "compressed_layers": Lc, "n_keep": n_keep, "parallelism": "none (1 GPU)"},
+        "encode_GBps": round(kv_enc / ((phase["score_evict"] + phase["encode"]) * 1e-3) / 1e9, 2),
+        "decode_GBps": round(kv_dec / (phase["decode"] * 1e-3) / 1e9, 2),
+        "phase_ms": {k: round(v, 4) for k, v in phase.items()},
+        "algorithmic_frac_of_peak": {
+            k: round(alg[k] / (phase[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) for k in phase},
+        "step_algorithmic_frac_of_peak": round(sum(alg.values()) / (ms_step * 1e-3) / 1e9
+                                               / HBM_PEAK_GBPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_layers, Lc))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -90,8 +90,7 @@ ScoreWs score_ws(const nq_params *p, void *base)
 int32_t codec_tiles(const nq_params *p) { return (keep_count(p) + nq::kCodecTile - 1) / nq::kCodecTile; }
 
 struct DecodeWs {
-    uint32_t *flag, *ticket;
-    uint2 *agg, *incl;
+    uint32_t *ticket, *agg, *incl;
     size_t bytes;
     int32_t tiles;
 };
@@ -100,16 +99,14 @@ DecodeWs decode_ws(const nq_params *p, void *base)
 {
     DecodeWs w;
     w.tiles = compressed_layers(p) * 2 * p->kv_heads * codec_tiles(p);
-    const size_t nt = (size_t)w.tiles;
-    const size_t f = align_up((nt + 1) * sizeof(uint32_t));
+    const size_t words = (size_t)w.tiles * 16 * 4;
     const size_t t = align_up(2 * sizeof(uint32_t));
-    const size_t v = align_up(nt * 16 * sizeof(uint2));
+    const size_t v = align_up(words * sizeof(uint32_t));
     char *b = (char *)base;
-    w.flag = (uint32_t *)b;
-    w.ticket = (uint32_t *)(b + f);
-    w.agg = (uint2 *)(b + f + t);
-    w.incl = (uint2 *)(b + f + t + v);
-    w.bytes = f + t + 2 * v;
+    w.ticket = (uint32_t *)b;
+    w.agg = (uint32_t *)(b + t);
+    w.incl = (uint32_t *)(b + t + v);   // directly follows agg: one reset covers both
+    w.bytes = t + 2 * v;
     return w;
 }
 
@@ -303,14 +300,14 @@ nq_status nq_decode(const nq_params *p, const int8_t *codes_k, const int8_t *cod
     a.out_k = K_out;
     a.out_v = V_out;
     a.out_f32 = out_dtype == NQ_OUT_F32;
-    a.lb_flag = w.flag;
     a.lb_ticket = w.ticket;
     a.lb_agg = w.agg;
     a.lb_incl = w.incl;
     hipStream_t s = as_stream(stream);
     clear_error();
-    hipLaunchKernelGGL(nq::k_decode_reset, dim3((w.tiles + 255) / 256 + 1), dim3(256), 0, s,
-                       w.flag, w.tiles, w.ticket);
+    const int64_t words = (int64_t)(w.incl - w.agg) + (int64_t)w.tiles * 64;
+    hipLaunchKernelGGL(nq::k_decode_reset, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0, s,
+                       w.agg, words, w.ticket);
     hipLaunchKernelGGL(nq::k_decode, dim3((uint32_t)w.tiles), dim3(nq::kCodecThreads), 0, s, a);
     return launched("nq_decode");
 }

@@ -27,8 +27,7 @@ struct CodecArgs {
     int8_t *codes_k, *codes_v;     // [Lc][H][n_keep][128]
     uint16_t *scales_k, *scales_v; // fp16 bits [Lc][H][n_keep][16]
     void *out_k, *out_v;           // decode outputs [Lc][H][n_keep][128]
-    uint32_t *lb_flag;             // decode look-back: per tile status (0 none, 1 agg, 2 incl)
-    uint2 *lb_agg, *lb_incl;       // [tiles][16] byte-wise sums of one tile / of its prefix
+    uint32_t *lb_agg, *lb_incl;    // decode look-back words [tiles][16 lanes][4] (see below)
     uint32_t *lb_ticket;           // [0]: tile ticket counter, [1]: spin-limit error flag
     int32_t H, T, layer_begin, n_keep;
     int32_t tiles_per_chain;
@@ -280,14 +279,44 @@ __global__ __launch_bounds__(kCodecThreads) void k_encode(CodecArgs a)
 // their own byte-wise sum and then their inclusive prefix (single-pass chained scan with
 // decoupled look-back). Tiles take tickets from an atomic counter in launch order, so every
 // tile a tile waits for has already started and makes progress.
+//
+// Publication needs no memory fence: a tile's 128-byte value is written as 64 words of
+// (tag << 16 | 16 payload bits) with relaxed device-scope atomic stores, tag 1 for the tile
+// sum and 2 for the inclusive prefix, into buffers zeroed before the launch. A reader takes a
+// value only once all 64 of its words carry the expected tag, so it can never combine a
+// half-written value, whatever order the stores become visible in. (A release/acquire pair
+// would write back and invalidate the whole L2 of the XCD on every publication.)
 // ---------------------------------------------------------------------------------------------
 constexpr uint32_t kSpinLimit = 1u << 26;
 
-__global__ void k_decode_reset(uint32_t *flag, int n, uint32_t *ticket)
+__global__ void k_decode_reset(uint32_t *words, int64_t n, uint32_t *ticket)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) flag[i] = 0u;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) words[i] = 0u;
     if (i < 2) ticket[i] = 0u;
+}
+
+__device__ __forceinline__ void lb_publish(uint32_t *base, uint2 v, uint32_t tag)
+{
+    const uint32_t t = tag << 16;
+    __hip_atomic_store(base + 0, t | (v.x & 0xffffu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(base + 1, t | (v.x >> 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(base + 2, t | (v.y & 0xffffu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(base + 3, t | (v.y >> 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// reads one lane's part of a published value; true if all four words carry the tag
+__device__ __forceinline__ bool lb_read(const uint32_t *base, uint32_t tag, uint2 &v)
+{
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++)
+        w[k] = __hip_atomic_load(const_cast<uint32_t *>(base) + k, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    v.x = (w[0] & 0xffffu) | (w[1] << 16);
+    v.y = (w[2] & 0xffffu) | (w[3] << 16);
+    return (w[0] >> 16) == tag && (w[1] >> 16) == tag && (w[2] >> 16) == tag &&
+           (w[3] >> 16) == tag;
 }
 
 template <bool IS_KEY>
@@ -374,40 +403,39 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
         const uint2 t = s_tot[k][g];
         gp = make_uint2(add_bytes(gp.x, t.x), add_bytes(gp.y, t.y));
     }
-    // 3. decoupled look-back, done by lane group 15 (it holds the tile total)
+    // 3. decoupled look-back, done by lane group 15 (it holds the tile total); the 16 lanes of
+    //    the group move together: a value is taken only when every lane's words are complete
     if (q == 15) {
         const uint2 agg = make_uint2(add_bytes(gp.x, acc.x), add_bytes(gp.y, acc.y));
         uint2 excl = make_uint2(0u, 0u);
+        const size_t me = ((size_t)ticket * 16 + g) * 4;
         if (tile == 0) {
-            a.lb_incl[(size_t)ticket * 16 + g] = agg;
-            __threadfence();
-            if (g == 0) __hip_atomic_store(&a.lb_flag[ticket], 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            lb_publish(a.lb_incl + me, agg, 2u);
         } else {
-            a.lb_agg[(size_t)ticket * 16 + g] = agg;
-            __threadfence();
-            if (g == 0) __hip_atomic_store(&a.lb_flag[ticket], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            lb_publish(a.lb_agg + me, agg, 1u);
             int pred = ticket - 1;
             uint32_t spins = 0;
             while (true) {
-                uint32_t f = __hip_atomic_load(&a.lb_flag[pred], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-                f = __builtin_amdgcn_readfirstlane(f);
-                if (f == 0u) {
-                    if (++spins > kSpinLimit) {   // never expected: report and give up
-                        if (g == 0) atomicOr(&a.lb_ticket[1], 1u);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
+                const size_t pw = ((size_t)pred * 16 + g) * 4;
+                uint2 v;
+                if (__ballot(!lb_read(a.lb_incl + pw, 2u, v)) == 0ull) {
+                    excl = make_uint2(add_bytes(excl.x, v.x), add_bytes(excl.y, v.y));
+                    break;
+                }
+                if (__ballot(!lb_read(a.lb_agg + pw, 1u, v)) == 0ull) {
+                    excl = make_uint2(add_bytes(excl.x, v.x), add_bytes(excl.y, v.y));
+                    pred--;
+                    spins = 0;
                     continue;
                 }
-                const uint2 v = (f == 2u) ? a.lb_incl[(size_t)pred * 16 + g] : a.lb_agg[(size_t)pred * 16 + g];
-                excl = make_uint2(add_bytes(excl.x, v.x), add_bytes(excl.y, v.y));
-                if (f == 2u) break;
-                pred--;
+                if (++spins > kSpinLimit) {   // never expected: report and give up the wait
+                    if (g == 0) atomicOr(&a.lb_ticket[1], 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
             }
-            const uint2 incl = make_uint2(add_bytes(excl.x, agg.x), add_bytes(excl.y, agg.y));
-            a.lb_incl[(size_t)ticket * 16 + g] = incl;
-            __threadfence();
-            if (g == 0) __hip_atomic_store(&a.lb_flag[ticket], 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            lb_publish(a.lb_incl + me,
+                       make_uint2(add_bytes(excl.x, agg.x), add_bytes(excl.y, agg.y)), 2u);
         }
         s_excl[g] = excl;
     }

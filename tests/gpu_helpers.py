@@ -87,11 +87,8 @@ class GpuRun:
 
     def lookback_error(self) -> int:
         """Spin-limit flag of the decode's tile look-back (0 when every wait ended normally)."""
-        ws = self.dws.cpu().numpy().view(np.uint32)
-        Lc = self.p.layer_end - self.p.layer_begin
-        tiles = Lc * 2 * self.p.kv_heads * ((self.n_keep + 255) // 256)
-        off = ((tiles + 1) * 4 + 255) // 256 * 256 // 4
-        return int(ws[off + 1])
+        ws = self.dws[:8].cpu().numpy().view(np.uint32)   # [0] ticket, [1] error flag
+        return int(ws[1])
 
 
 def absolute_codes(d: np.ndarray) -> np.ndarray:
