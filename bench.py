@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=4,
                     help="layers of the workload the CPU oracle baseline processes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one plain device copy of this many MiB (a known-size "
+                         "kernel that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                       "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -132,6 +135,13 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs generated and uploaded in {time.time() - t0:.1f}s")
 
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cos, sin = nq.rope_table(p, dev)
     positions = torch.empty((Lc, n_keep), dtype=torch.int32, device=dev)
     ws_s = nq.workspace(nq.nq_score_evict_workspace_bytes(p), dev)

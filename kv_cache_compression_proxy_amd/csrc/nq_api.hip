@@ -242,6 +242,8 @@ static nq::CodecArgs codec_args(const nq_params *p, const int32_t *positions,
     a.tiles_per_chain = codec_tiles(p);
     a.rho_k = rho_of(p->bits_k);
     a.rho_v = rho_of(p->bits_v);
+    a.rho_inv_k = 1.0f / a.rho_k;   // IEEE division on the host: the nearest fp32
+    a.rho_inv_v = 1.0f / a.rho_v;
     return a;
 }
 

@@ -32,6 +32,7 @@ struct CodecArgs {
     int32_t H, T, layer_begin, n_keep;
     int32_t tiles_per_chain;
     float rho_k, rho_v;
+    float rho_inv_k, rho_inv_v;    // fp32 nearest to 1/rho
     int32_t out_f32;
 };
 
@@ -54,11 +55,18 @@ __global__ __launch_bounds__(256) void k_rope_table(RopeTheta th, int T, float *
     S[idx] = (float)sv;
 }
 
-// Normalised Hadamard transform of a row held as 8 values per lane (dims 8g + j), butterflies
-// in the order h = 1, 2, 4 (inside the lane) then 8, 16, 32, 64 (lane partners g^1, g^2, g^4,
-// g^8), pair (a, b) -> (a + b, a - b); then times fp32(1/sqrt(128)). Same fp32 results as the
-// sequential order: every butterfly output is one correctly rounded add or subtract.
-__device__ __forceinline__ void hadamard_rows(float x[8], int g)
+// Hadamard butterflies of a row held as 8 values per lane (dims 8g + j), in the order h = 1, 2,
+// 4 (inside the lane) then 8, 16, 32, 64 (lane partners g^1, g^2, g^4, g^8); pair (a, b) ->
+// (a + b, a - b). The normalisation by 1/sqrt(128) is left to the caller.
+//
+// Cross-lane stages keep a per-lane sign: each lane computes self + sgn * partner with one
+// fused DPP multiply-add (sgn = +1 in the lower lane of a pair, -1 in the upper one), so the
+// upper lane holds -(a - b). By induction every lane ends holding lane_sign(g) times the true
+// value, lane_sign(g) = (-1)^popcount(g); each value is one correctly rounded add or subtract
+// of the same operands as in the sequential order, so |values| match it bit for bit.
+__device__ __forceinline__ float lane_sign(int g) { return (__popc(g & 15) & 1) ? -1.0f : 1.0f; }
+
+__device__ __forceinline__ void hadamard_butterflies(float x[8], int g)
 {
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
@@ -71,17 +79,44 @@ __device__ __forceinline__ void hadamard_rows(float x[8], int g)
             }
         }
     }
+    const float s1 = (g & 1) ? -1.0f : 1.0f, s2 = (g & 2) ? -1.0f : 1.0f;
+    const float s4 = (g & 4) ? -1.0f : 1.0f, s8 = (g & 8) ? -1.0f : 1.0f;
+    // x[j] += s * x[j] of the partner lane: v_fmac_f32 with a DPP-routed first operand (the
+    // compiler does not fuse a DPP move into fmac by itself). s_nop 1 gives the two wait states
+    // a DPP read needs after a VALU write of the same register.
+#define NQ_FMAC_DPP(CTRL)                                                                      \
+    "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"             \
+    "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"             \
+    "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"             \
+    "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"             \
+    "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"             \
+    "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"             \
+    "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"             \
+    "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+#define NQ_X8 "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7])
+    asm("s_nop 1\n" NQ_FMAC_DPP("quad_perm:[1,0,3,2]") : NQ_X8 : "v"(s1));
+    asm("s_nop 1\n" NQ_FMAC_DPP("quad_perm:[2,3,0,1]") : NQ_X8 : "v"(s2));
+    {
+        // lane ^ 4 = row_half_mirror (lane ^ 7) of quad_perm [3,2,1,0] (lane ^ 3)
+        float t[8];
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-        const bool upper = (g & m) != 0;
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const float o = __shfl_xor(x[j], m);
-            x[j] = upper ? (o - x[j]) : (x[j] + o);
-        }
+        for (int j = 0; j < 8; j++) t[j] = dpp<kDppXor3>(x[j]);
+        asm("s_nop 1\n"
+            "v_fmac_f32_dpp %0, %8, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+            "v_fmac_f32_dpp %1, %9, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+            "v_fmac_f32_dpp %2, %10, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+            "v_fmac_f32_dpp %3, %11, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+            "v_fmac_f32_dpp %4, %12, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+            "v_fmac_f32_dpp %5, %13, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+            "v_fmac_f32_dpp %6, %14, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+            "v_fmac_f32_dpp %7, %15, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+            : NQ_X8
+            : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(t[4]), "v"(t[5]), "v"(t[6]),
+              "v"(t[7]), "v"(s4));
     }
-#pragma unroll
-    for (int j = 0; j < 8; j++) x[j] = x[j] * kInvSqrt128;
+    asm("s_nop 1\n" NQ_FMAC_DPP("row_ror:8") : NQ_X8 : "v"(s8));
+#undef NQ_X8
+#undef NQ_FMAC_DPP
 }
 
 // Smallest fp16 >= v (v > 0 finite), saturating at 65504.
@@ -106,26 +141,27 @@ __device__ __forceinline__ void e8_nearest_code(const float u[8], uint32_t &w0, 
 {
     float f[8], e[8];
     uint32_t kmax = 0u, kmin = 0xffffffffu, sx = 0u;
-    float sf = 0.0f, A2 = 0.0f, Sa = 0.0f;
+    float sf = 0.0f, Sa = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         f[i] = __builtin_rintf(u[i]);
         e[i] = u[i] - f[i];
-        const uint32_t ab = __float_as_uint(e[i]) & 0x7ffffff8u;
-        kmax = max(kmax, ab | (7u - (uint32_t)i));
-        kmin = min(kmin, ab | (uint32_t)i);
-        sx ^= __float_as_uint(e[i]);
+        const uint32_t eb = __float_as_uint(e[i]);
+        kmax = max(kmax, (eb & 0x7ffffff8u) | (7u - (uint32_t)i));
+        kmin = min(kmin, (eb & 0x7ffffff8u) | (uint32_t)i);
+        sx ^= eb;
         sf += f[i];
-        A2 = __builtin_fmaf(e[i], e[i], A2);
         Sa += __builtin_fabsf(e[i]);
     }
     const int P0 = ((int)sf) & 1;
     const int P1 = P0 ^ (int)(sx >> 31);
     const float amax = __uint_as_float(kmax & ~7u);
     const float amin = __uint_as_float(kmin & ~7u);
-    const float d0 = P0 ? A2 + (1.0f - 2.0f * amax) : A2;
-    const float d1 = (2.0f - Sa + A2) + (P1 ? 2.0f * amin : 0.0f);
-    const bool half = d1 < d0;
+    // d1 - d0 = (2 - sum a + [P1] 2 min a) - [P0] (1 - 2 max a); sum(a^2) cancels
+    float dd = 2.0f - Sa;
+    if (P1) dd = __builtin_fmaf(2.0f, amin, dd);
+    if (P0) dd = __builtin_fmaf(2.0f, amax, dd - 1.0f);
+    const bool half = dd < 0.0f;
     const int jf = half ? (int)(kmin & 7u) : (int)(7u - (kmax & 7u));
     const int par = half ? P1 : P0;
     // e at index jf (select tree)
@@ -162,7 +198,7 @@ __device__ __forceinline__ void e8_nearest_code(const float u[8], uint32_t &w0, 
 template <bool IS_KEY>
 __device__ __forceinline__ uint2 encode_token(const CodecArgs &a, const uint16_t *__restrict__ X,
                                               const int32_t *__restrict__ pos, int j, int g,
-                                              float rho, uint32_t &s16)
+                                              float rho, float rho_inv, uint32_t &s16)
 {
     int p = pos[j];
     p = min(max(p, 0), a.T - 1);
@@ -174,29 +210,43 @@ __device__ __forceinline__ uint2 encode_token(const CodecArgs &a, const uint16_t
         float c[8], s[8];
         load_f32x8(a.rope_cos + (size_t)p * 64 + 8 * (g & 7), c);
         load_f32x8(a.rope_sin + (size_t)p * 64 + 8 * (g & 7), s);
-        const bool upper = g >= 8;
+        const float sg = g >= 8 ? -1.0f : 1.0f;
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-            const float o = __shfl_xor(x[k], 8);
             const float t1 = x[k] * c[k];
-            const float t2 = o * s[k];
-            x[k] = upper ? t1 - t2 : t1 + t2;
+            const float t2 = lane_xor8(x[k]) * s[k];
+            x[k] = __builtin_fmaf(sg, t2, t1);        // t1 +- t2, rounded once
         }
     }
-    hadamard_rows(x, g);
+    hadamard_butterflies(x, g);
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; k++) amax = fmaxf(amax, __builtin_fabsf(x[k]));
+    // the normalised row is x * fp32(1/sqrt(128)); rounding is monotone, so the group's
+    // largest normalised magnitude is the rounded product of the largest raw one
+    amax = amax * kInvSqrt128;
     float u[8];
     if (amax == 0.0f) {
         s16 = 0u;
 #pragma unroll
         for (int k = 0; k < 8; k++) u[k] = 0.0f;
     } else {
-        s16 = f16_ceil_bits(amax / rho);
-        const float s = h2f(s16);
+        // amax / rho correctly rounded: q = amax * (1/rho), then one remainder correction
+        // (Markstein: with 1/rho rounded to nearest and q within an ulp, the corrected
+        // quotient is the correctly rounded one)
+        const float q0 = amax * rho_inv;
+        const float rem = __builtin_fmaf(-q0, rho, amax);
+        s16 = f16_ceil_bits(__builtin_fmaf(rem, rho_inv, q0));
+        // u = x / s up to a few ulps (x * (c * rcp(s)) instead of (x * c) / s): only a point
+        // within ~1e-6 of a Voronoi facet can change lattice point, and such points are ties
+        // (the butterflies leave lane_sign(g) times the row in x; the factor restores the sign)
+        const float f = (kInvSqrt128 * lane_sign(g)) * __builtin_amdgcn_rcpf(h2f(s16));
 #pragma unroll
-        for (int k = 0; k < 8; k++) u[k] = fminf(fmaxf(x[k] / s, -rho), rho);
+        for (int k = 0; k < 8; k++) u[k] = x[k] * f;
+        if (s16 == 0x7bffu) {   // saturated scale: |x / s| may exceed rho
+#pragma unroll
+            for (int k = 0; k < 8; k++) u[k] = fminf(fmaxf(u[k], -rho), rho);
+        }
     }
     uint2 c;
     e8_nearest_code(u, c.x, c.y);
@@ -225,6 +275,7 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile)
     int8_t *codes = (IS_KEY ? a.codes_k : a.codes_v) + chain * (size_t)n_keep * kHeadDim + 8 * g;
     uint16_t *scales = (IS_KEY ? a.scales_k : a.scales_v) + chain * (size_t)n_keep * kGroups + g;
     const float rho = IS_KEY ? a.rho_k : a.rho_v;
+    const float rho_inv = IS_KEY ? a.rho_inv_k : a.rho_inv_v;
     const uint2 zero = make_uint2(0x40404040u, 0x40404040u);   // code 0 in offset form
 
     // the tile's predecessor token, coded (not stored) by lane group 0
@@ -233,7 +284,7 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile)
         const int jh = tile * kCodecTile - 1;
         if (jh >= 0) {
             uint32_t s16;
-            hc = encode_token<IS_KEY>(a, X, pos, jh, g, rho, s16);
+            hc = encode_token<IS_KEY>(a, X, pos, jh, g, rho, rho_inv, s16);
         }
         s_last[0][g] = hc;
     }
@@ -243,7 +294,7 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile)
         const int j = j0 + i;
         if (j < n_keep) {
             uint32_t s16;
-            const uint2 c = encode_token<IS_KEY>(a, X, pos, j, g, rho, s16);
+            const uint2 c = encode_token<IS_KEY>(a, X, pos, j, g, rho, rho_inv, s16);
             scales[(size_t)j * kGroups] = (uint16_t)s16;
             if (i == 0)
                 first = c;
@@ -319,14 +370,16 @@ __device__ __forceinline__ bool lb_read(const uint32_t *base, uint32_t tag, uint
            (w[3] >> 16) == tag;
 }
 
+// Reconstructs one token of one chain for this lane's 8 dims and stores it. c: the token's
+// absolute code bytes (two's complement), s16: this group's scale, (cr, sr): the rotary table row
+// of the token's position (keys only).
 template <bool IS_KEY>
 __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off, int j, int g,
-                                             const int32_t *__restrict__ pos, uint2 code,
-                                             uint32_t s16)
+                                             uint2 code, uint32_t s16, const float cr[8],
+                                             const float sr[8])
 {
-    // code bytes are two's complement c; x = s * c / 2 (exact in fp32)
-    const float s = h2f(s16);
-    const float hs = 0.5f * s, off = -64.0f * s;
+    // x = s * c / 2 times the Hadamard normalisation, as fma(scale, c + 128, -128 * scale)
+    const float hs = (0.5f * kInvSqrt128) * h2f(s16), off = -128.0f * hs;
     const uint32_t ub0 = code.x ^ 0x80808080u, ub1 = code.y ^ 0x80808080u;   // c + 128
     float x[8];
     x[0] = __builtin_fmaf(hs, (float)(ub0 & 0xffu), off);
@@ -337,52 +390,64 @@ __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off,
     x[5] = __builtin_fmaf(hs, (float)((ub1 >> 8) & 0xffu), off);
     x[6] = __builtin_fmaf(hs, (float)((ub1 >> 16) & 0xffu), off);
     x[7] = __builtin_fmaf(hs, (float)((ub1 >> 24) & 0xffu), off);
-    hadamard_rows(x, g);
+    hadamard_butterflies(x, g);   // x = lane_sign(g) * (the reconstructed row)
     if (IS_KEY) {
-        // RoPE at the stored position: k_i = x_i*C - x_{i+64}*S, k_{i+64} = x_{i+64}*C + x_i*S
-        int p = pos[j];
-        p = min(max(p, 0), a.T - 1);
-        float c[8], sn[8];
-        load_f32x8(a.rope_cos + (size_t)p * 64 + 8 * (g & 7), c);
-        load_f32x8(a.rope_sin + (size_t)p * 64 + 8 * (g & 7), sn);
-        const bool upper = g >= 8;
+        // RoPE at the stored position: k_i = x_i*C - x_{i+64}*S, k_{i+64} = x_{i+64}*C + x_i*S.
+        // The partner lane g^8 carries the opposite lane sign, hence the flipped +-.
+        const float sg = g >= 8 ? -1.0f : 1.0f;
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const float o = __shfl_xor(x[k], 8);
-            const float t1 = x[k] * c[k];
-            const float t2 = o * sn[k];
-            x[k] = upper ? t1 + t2 : t1 - t2;
-        }
+        for (int k = 0; k < 8; k++)
+            x[k] = __builtin_fmaf(sg, lane_xor8(x[k]) * sr[k], x[k] * cr[k]);
     }
+    const uint32_t sbit = (__popc(g & 15) & 1) ? 0x80000000u : 0u;   // lane_sign as a sign bit
     const size_t o = row_off + (size_t)j * kHeadDim + 8 * g;
     if (a.out_f32) {
         float *dst = (float *)(IS_KEY ? a.out_k : a.out_v) + o;
+#pragma unroll
+        for (int k = 0; k < 8; k++) x[k] = __uint_as_float(__float_as_uint(x[k]) ^ sbit);
         *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
         *reinterpret_cast<float4 *>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
     } else {
+        // rounding to fp16 commutes with the sign, which is flipped on the packed halves
         uint16_t *dst = (uint16_t *)(IS_KEY ? a.out_k : a.out_v) + o;
+        const uint32_t s2 = sbit | (sbit >> 16);
         uint4 v;
-        v.x = (uint32_t)f2h_bits(x[0]) | ((uint32_t)f2h_bits(x[1]) << 16);
-        v.y = (uint32_t)f2h_bits(x[2]) | ((uint32_t)f2h_bits(x[3]) << 16);
-        v.z = (uint32_t)f2h_bits(x[4]) | ((uint32_t)f2h_bits(x[5]) << 16);
-        v.w = (uint32_t)f2h_bits(x[6]) | ((uint32_t)f2h_bits(x[7]) << 16);
+        v.x = ((uint32_t)f2h_bits(x[0]) | ((uint32_t)f2h_bits(x[1]) << 16)) ^ s2;
+        v.y = ((uint32_t)f2h_bits(x[2]) | ((uint32_t)f2h_bits(x[3]) << 16)) ^ s2;
+        v.z = ((uint32_t)f2h_bits(x[4]) | ((uint32_t)f2h_bits(x[5]) << 16)) ^ s2;
+        v.w = ((uint32_t)f2h_bits(x[6]) | ((uint32_t)f2h_bits(x[7]) << 16)) ^ s2;
         *reinterpret_cast<uint4 *>(dst) = v;
     }
 }
 
 template <bool IS_KEY>
-__device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int ticket)
+__device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int ticket, int chains)
 {
     __shared__ uint2 s_tot[16][16];
     __shared__ uint2 s_excl[16];
+    __shared__ int32_t s_pos[kCodecTile];
+    __shared__ uint4 s_scale[kCodecTile * kGroups * 2 / 16];   // the tile's fp16 scales
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 15, q = wave * 4 + (lane >> 4);
     const int n_keep = a.n_keep;
     const size_t chain = (size_t)lc * a.H + h;
     const int8_t *codes = (IS_KEY ? a.codes_k : a.codes_v) + chain * (size_t)n_keep * kHeadDim + 8 * g;
-    const uint16_t *scales = (IS_KEY ? a.scales_k : a.scales_v) + chain * (size_t)n_keep * kGroups + g;
-    const int32_t *pos = a.positions + (size_t)lc * n_keep;
-    const int j0 = tile * kCodecTile + q * kCodecRun;
+    const int t0 = tile * kCodecTile;
+    const int nt = min(kCodecTile, n_keep - t0);
+    const int j0 = t0 + q * kCodecRun;
+
+    // 0. stage the tile's positions and scales in LDS with coalesced loads; they arrive while the
+    //    running sum and the look-back below proceed
+    {
+        const uint4 *sc = reinterpret_cast<const uint4 *>(
+            (IS_KEY ? a.scales_k : a.scales_v) + (chain * (size_t)n_keep + t0) * kGroups);
+        for (int c = threadIdx.x; c < 2 * nt; c += kCodecThreads) s_scale[c] = sc[c];
+        if (IS_KEY) {
+            const int32_t *pos = a.positions + (size_t)lc * n_keep + t0;
+            for (int i = threadIdx.x; i < nt; i += kCodecThreads)
+                s_pos[i] = min(max(pos[i], 0), a.T - 1);
+        }
+    }
 
     // 1. this lane group's deltas and their running sum
     uint2 run[kCodecRun];
@@ -413,7 +478,7 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
             lb_publish(a.lb_incl + me, agg, 2u);
         } else {
             lb_publish(a.lb_agg + me, agg, 1u);
-            int pred = ticket - 1;
+            int pred = ticket - chains;          // the previous tile of this chain
             uint32_t spins = 0;
             while (true) {
                 const size_t pw = ((size_t)pred * 16 + g) * 4;
@@ -424,7 +489,7 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
                 }
                 if (__ballot(!lb_read(a.lb_agg + pw, 1u, v)) == 0ull) {
                     excl = make_uint2(add_bytes(excl.x, v.x), add_bytes(excl.y, v.y));
-                    pred--;
+                    pred -= chains;
                     spins = 0;
                     continue;
                 }
@@ -442,37 +507,59 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
     __syncthreads();
     const uint2 base0 = s_excl[g];
     const uint2 base = make_uint2(add_bytes(base0.x, gp.x), add_bytes(base0.y, gp.y));
-    // 4. reconstruct every token of this lane group
+    // 4. reconstruct every token of this lane group; the next token's rotary rows are requested
+    //    before the current token is computed
     const size_t row_off = chain * (size_t)n_keep * kHeadDim;
+    const uint16_t *sl = reinterpret_cast<const uint16_t *>(s_scale);
+    const int jend = min(n_keep, j0 + kCodecRun);
+    float cn[8], sn[8];
+    if (IS_KEY && j0 < jend) {
+        const size_t p = (size_t)s_pos[j0 - t0] * 64 + 8 * (g & 7);
+        load_f32x8(a.rope_cos + p, cn);
+        load_f32x8(a.rope_sin + p, sn);
+    }
 #pragma unroll
     for (int i = 0; i < kCodecRun; i++) {
         const int j = j0 + i;
-        if (j < n_keep) {
+        if (j < jend) {
+            float cr[8], sr[8];
+            if (IS_KEY) {
+#pragma unroll
+                for (int k = 0; k < 8; k++) { cr[k] = cn[k]; sr[k] = sn[k]; }
+                if (j + 1 < jend) {
+                    const size_t p = (size_t)s_pos[j + 1 - t0] * 64 + 8 * (g & 7);
+                    load_f32x8(a.rope_cos + p, cn);
+                    load_f32x8(a.rope_sin + p, sn);
+                }
+            }
             const uint2 c = make_uint2(add_bytes(base.x, run[i].x), add_bytes(base.y, run[i].y));
-            const uint32_t s16 = scales[(size_t)j * kGroups];
-            decode_store<IS_KEY>(a, row_off, j, g, pos, c, s16);
+            decode_store<IS_KEY>(a, row_off, j, g, c, sl[(j - t0) * kGroups + g], cr, sr);
         }
     }
 }
 
 // grid: Lc * 2 * H * tiles_per_chain blocks; the logical tile comes from the ticket, ordered
-// chain-major so a tile's predecessors in its chain hold smaller tickets.
+// tile-major over the chains: tile k of a chain holds ticket k * chains + chain, so its
+// predecessor started `chains` tickets earlier and has usually published its inclusive prefix
+// by the time it is looked up (a chain-major order would start a chain's tiles together and
+// make the last ones walk back through many tile sums).
 __global__ __launch_bounds__(kCodecThreads) void k_decode(CodecArgs a)
 {
     __shared__ int s_ticket;
     if (threadIdx.x == 0) s_ticket = (int)atomicAdd(&a.lb_ticket[0], 1u);
     __syncthreads();
     const int ticket = s_ticket;
-    const int tile = ticket % a.tiles_per_chain;
-    uint32_t r = ticket / a.tiles_per_chain;
+    const int chains = (int)(gridDim.x / (uint32_t)a.tiles_per_chain);
+    const int tile = ticket / chains;
+    uint32_t r = ticket % chains;
     const int h = r % a.H;
     r /= a.H;
     const int tensor = r & 1;
     const int lc = r >> 1;
     if (tensor == 0)
-        decode_tile<true>(a, lc, h, tile, ticket);
+        decode_tile<true>(a, lc, h, tile, ticket, chains);
     else
-        decode_tile<false>(a, lc, h, tile, ticket);
+        decode_tile<false>(a, lc, h, tile, ticket, chains);
 }
 
 }  // namespace nq
