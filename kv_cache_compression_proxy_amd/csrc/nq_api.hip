@@ -40,7 +40,7 @@ nq_status check(const nq_params *p)
     if (p->bits_k > 4 || p->bits_v > 4) return NQ_ERR_UNSUPPORTED;
     // 32-bit token and tile indices inside the kernels
     if ((int64_t)p->tokens * 16 > INT32_MAX) return NQ_ERR_UNSUPPORTED;
-    if ((int64_t)p->kv_heads * 2 * compressed_layers(p) * ((int64_t)p->tokens / nq::kCodecTile + 1) >
+    if ((int64_t)p->kv_heads * 2 * compressed_layers(p) * ((int64_t)p->tokens / nq::kDecTile + 1) >
         INT32_MAX)
         return NQ_ERR_UNSUPPORTED;
     return NQ_OK;
@@ -88,6 +88,7 @@ ScoreWs score_ws(const nq_params *p, void *base)
 }
 
 int32_t codec_tiles(const nq_params *p) { return (keep_count(p) + nq::kCodecTile - 1) / nq::kCodecTile; }
+int32_t decode_tiles(const nq_params *p) { return (keep_count(p) + nq::kDecTile - 1) / nq::kDecTile; }
 
 struct DecodeWs {
     uint32_t *ticket, *agg, *incl;
@@ -98,7 +99,7 @@ struct DecodeWs {
 DecodeWs decode_ws(const nq_params *p, void *base)
 {
     DecodeWs w;
-    w.tiles = compressed_layers(p) * 2 * p->kv_heads * codec_tiles(p);
+    w.tiles = compressed_layers(p) * 2 * p->kv_heads * decode_tiles(p);
     const size_t words = (size_t)w.tiles * 16 * 4;
     const size_t t = align_up(2 * sizeof(uint32_t));
     const size_t v = align_up(words * sizeof(uint32_t));
@@ -240,6 +241,7 @@ static nq::CodecArgs codec_args(const nq_params *p, const int32_t *positions,
     a.layer_begin = p->layer_begin;
     a.n_keep = keep_count(p);
     a.tiles_per_chain = codec_tiles(p);
+    a.dec_tiles_per_chain = decode_tiles(p);
     a.rho_k = rho_of(p->bits_k);
     a.rho_v = rho_of(p->bits_v);
     a.rho_inv_k = 1.0f / a.rho_k;   // IEEE division on the host: the nearest fp32

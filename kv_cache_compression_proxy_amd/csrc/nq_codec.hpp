@@ -17,8 +17,10 @@
 namespace nq {
 
 constexpr int kCodecThreads = 256;
-constexpr int kCodecRun = 16;                          // tokens walked per lane group
-constexpr int kCodecTile = 16 * kCodecRun;             // tokens per workgroup tile
+constexpr int kCodecRun = 16;                          // encode: tokens walked per lane group
+constexpr int kCodecTile = 16 * kCodecRun;             // encode: tokens per workgroup tile
+constexpr int kDecRun = 8;                             // decode: tokens per lane group
+constexpr int kDecTile = 16 * kDecRun;                 // decode: tokens per workgroup tile
 
 struct CodecArgs {
     const uint16_t *K, *V;         // fp16 [L][H][T][128]
@@ -30,7 +32,8 @@ struct CodecArgs {
     uint32_t *lb_agg, *lb_incl;    // decode look-back words [tiles][16 lanes][4] (see below)
     uint32_t *lb_ticket;           // [0]: tile ticket counter, [1]: spin-limit error flag
     int32_t H, T, layer_begin, n_keep;
-    int32_t tiles_per_chain;
+    int32_t tiles_per_chain;       // encode tiles (kCodecTile tokens) per chain
+    int32_t dec_tiles_per_chain;   // decode tiles (kDecTile tokens) per chain
     float rho_k, rho_v;
     float rho_inv_k, rho_inv_v;    // fp32 nearest to 1/rho
     int32_t out_f32;
@@ -261,10 +264,16 @@ __device__ __forceinline__ uint2 delta_code(uint2 cur, uint2 prev)
                       ((cur.y + 0x80808080u) - prev.y) ^ 0x80808080u);
 }
 
+struct EncodeShared {
+    uint2 last[17][16];                         // predecessor codes of each lane group
+    uint4 scales[kCodecTile * kGroups * 2 / 16];   // the tile's fp16 scales, stored coalesced
+};
+
 template <bool IS_KEY>
-__device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile)
+__device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeShared &sh)
 {
-    __shared__ uint2 s_last[17][16];
+    auto &s_last = sh.last;
+    uint16_t *s_sc = reinterpret_cast<uint16_t *>(sh.scales);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 15, q = wave * 4 + (lane >> 4);
     const int n_keep = a.n_keep;
@@ -273,7 +282,7 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile)
                         ((size_t)(a.layer_begin + lc) * a.H + h) * (size_t)a.T * kHeadDim + 8 * g;
     const int32_t *pos = a.positions + (size_t)lc * n_keep;
     int8_t *codes = (IS_KEY ? a.codes_k : a.codes_v) + chain * (size_t)n_keep * kHeadDim + 8 * g;
-    uint16_t *scales = (IS_KEY ? a.scales_k : a.scales_v) + chain * (size_t)n_keep * kGroups + g;
+    const int t0 = tile * kCodecTile;
     const float rho = IS_KEY ? a.rho_k : a.rho_v;
     const float rho_inv = IS_KEY ? a.rho_inv_k : a.rho_inv_v;
     const uint2 zero = make_uint2(0x40404040u, 0x40404040u);   // code 0 in offset form
@@ -295,7 +304,7 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile)
         if (j < n_keep) {
             uint32_t s16;
             const uint2 c = encode_token<IS_KEY>(a, X, pos, j, g, rho, rho_inv, s16);
-            scales[(size_t)j * kGroups] = (uint16_t)s16;
+            s_sc[(j - t0) * kGroups + g] = (uint16_t)s16;
             if (i == 0)
                 first = c;
             else
@@ -307,6 +316,11 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile)
     __syncthreads();
     if (j0 < n_keep)
         *reinterpret_cast<uint2 *>(codes + (size_t)j0 * kHeadDim) = delta_code(first, s_last[q][g]);
+    // the tile's scales: 32 bytes per token, written as 16-byte chunks
+    const int nt = min(kCodecTile, n_keep - t0);
+    uint4 *sc = reinterpret_cast<uint4 *>((IS_KEY ? a.scales_k : a.scales_v) +
+                                          (chain * (size_t)n_keep + t0) * kGroups);
+    for (int c = threadIdx.x; c < 2 * nt; c += kCodecThreads) sc[c] = sh.scales[c];
 }
 
 // grid: Lc * 2 * H * tiles_per_chain blocks, XCD-aware order (heads of one token tile adjacent)
@@ -319,10 +333,11 @@ __global__ __launch_bounds__(kCodecThreads) void k_encode(CodecArgs a)
     r >>= 1;
     const int tile = r % a.tiles_per_chain;
     const int lc = r / a.tiles_per_chain;
+    __shared__ EncodeShared sh;
     if (tensor == 0)
-        encode_tile<true>(a, lc, h, tile);
+        encode_tile<true>(a, lc, h, tile, sh);
     else
-        encode_tile<false>(a, lc, h, tile);
+        encode_tile<false>(a, lc, h, tile, sh);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -370,17 +385,17 @@ __device__ __forceinline__ bool lb_read(const uint32_t *base, uint32_t tag, uint
            (w[3] >> 16) == tag;
 }
 
-// Reconstructs one token of one chain for this lane's 8 dims and stores it. c: the token's
-// absolute code bytes (two's complement), s16: this group's scale, (cr, sr): the rotary table row
-// of the token's position (keys only).
+// Reconstructs one token of one chain for this lane's 8 dims and stores it. code: the token's
+// absolute code bytes as c + 64, s16: this group's scale, (cr, sr): the rotary table row of the
+// token's position (keys only).
 template <bool IS_KEY>
 __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off, int j, int g,
                                              uint2 code, uint32_t s16, const float cr[8],
                                              const float sr[8])
 {
-    // x = s * c / 2 times the Hadamard normalisation, as fma(scale, c + 128, -128 * scale)
-    const float hs = (0.5f * kInvSqrt128) * h2f(s16), off = -128.0f * hs;
-    const uint32_t ub0 = code.x ^ 0x80808080u, ub1 = code.y ^ 0x80808080u;   // c + 128
+    // x = s * c / 2 times the Hadamard normalisation, as fma(scale, c + 64, -64 * scale)
+    const float hs = (0.5f * kInvSqrt128) * h2f(s16), off = -64.0f * hs;
+    const uint32_t ub0 = code.x, ub1 = code.y;
     float x[8];
     x[0] = __builtin_fmaf(hs, (float)(ub0 & 0xffu), off);
     x[1] = __builtin_fmaf(hs, (float)((ub0 >> 8) & 0xffu), off);
@@ -420,21 +435,29 @@ __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off,
     }
 }
 
+struct DecodeShared {
+    uint2 tot[16][16];                          // running-sum totals of the lane groups
+    uint2 excl[16];                             // the tile's exclusive prefix
+    int32_t pos[kDecTile];                      // the tile's positions
+    uint4 scale[kDecTile * kGroups * 2 / 16];     // the tile's fp16 scales
+    uint4 delta[kDecTile * kHeadDim / 16];        // the tile's delta codes
+};
+
 template <bool IS_KEY>
-__device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int ticket, int chains)
+__device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int ticket, int chains,
+                            DecodeShared &sh)
 {
-    __shared__ uint2 s_tot[16][16];
-    __shared__ uint2 s_excl[16];
-    __shared__ int32_t s_pos[kCodecTile];
-    __shared__ uint4 s_scale[kCodecTile * kGroups * 2 / 16];   // the tile's fp16 scales
+    auto &s_tot = sh.tot;
+    auto &s_excl = sh.excl;
+    auto &s_pos = sh.pos;
+    auto &s_scale = sh.scale;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 15, q = wave * 4 + (lane >> 4);
     const int n_keep = a.n_keep;
     const size_t chain = (size_t)lc * a.H + h;
-    const int8_t *codes = (IS_KEY ? a.codes_k : a.codes_v) + chain * (size_t)n_keep * kHeadDim + 8 * g;
-    const int t0 = tile * kCodecTile;
-    const int nt = min(kCodecTile, n_keep - t0);
-    const int j0 = t0 + q * kCodecRun;
+    const int t0 = tile * kDecTile;
+    const int nt = min(kDecTile, n_keep - t0);
+    const int j0 = t0 + q * kDecRun;
 
     // 0. stage the tile's positions and scales in LDS with coalesced loads; they arrive while the
     //    running sum and the look-back below proceed
@@ -442,6 +465,9 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
         const uint4 *sc = reinterpret_cast<const uint4 *>(
             (IS_KEY ? a.scales_k : a.scales_v) + (chain * (size_t)n_keep + t0) * kGroups);
         for (int c = threadIdx.x; c < 2 * nt; c += kCodecThreads) s_scale[c] = sc[c];
+        const uint4 *dc = reinterpret_cast<const uint4 *>(
+            (IS_KEY ? a.codes_k : a.codes_v) + (chain * (size_t)n_keep + t0) * kHeadDim);
+        for (int c = threadIdx.x; c < 8 * nt; c += kCodecThreads) sh.delta[c] = dc[c];
         if (IS_KEY) {
             const int32_t *pos = a.positions + (size_t)lc * n_keep + t0;
             for (int i = threadIdx.x; i < nt; i += kCodecThreads)
@@ -449,25 +475,32 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
         }
     }
 
-    // 1. this lane group's deltas and their running sum
-    uint2 run[kCodecRun];
+    // 1. the byte-wise sum of this lane group's deltas (from the staged tile)
+    __syncthreads();
+    const uint2 *sd = reinterpret_cast<const uint2 *>(sh.delta) + g;   // [token][16 lanes]
     uint2 acc = make_uint2(0u, 0u);
 #pragma unroll
-    for (int i = 0; i < kCodecRun; i++) {
-        const int j = j0 + i;
-        uint2 d = make_uint2(0u, 0u);
-        if (j < n_keep) d = *reinterpret_cast<const uint2 *>(codes + (size_t)j * kHeadDim);
-        acc = make_uint2(add_bytes(acc.x, d.x), add_bytes(acc.y, d.y));
-        run[i] = acc;
+    for (int i = 0; i < kDecRun; i++) {
+        const int jl = q * kDecRun + i;
+        if (jl < nt) {
+            const uint2 d = sd[jl * 16];
+            acc = make_uint2(add_bytes(acc.x, d.x), add_bytes(acc.y, d.y));
+        }
     }
-    s_tot[q][g] = acc;
-    __syncthreads();
-    // 2. prefix over the lane groups before this one, and the tile total (group 15's lanes)
-    uint2 gp = make_uint2(0u, 0u);
-    for (int k = 0; k < q; k++) {
-        const uint2 t = s_tot[k][g];
-        gp = make_uint2(add_bytes(gp.x, t.x), add_bytes(gp.y, t.y));
+    // 2. prefix over the lane groups before this one (log-step scan through LDS); group 15's
+    //    lanes then hold the tile total in gp + acc
+    uint2 incl = acc;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+        s_tot[q][g] = incl;
+        __syncthreads();
+        if (q >= d) {
+            const uint2 t = s_tot[q - d][g];
+            incl = make_uint2(add_bytes(incl.x, t.x), add_bytes(incl.y, t.y));
+        }
+        __syncthreads();
     }
+    const uint2 gp = make_uint2(sub_bytes(incl.x, acc.x), sub_bytes(incl.y, acc.y));
     // 3. decoupled look-back, done by lane group 15 (it holds the tile total); the 16 lanes of
     //    the group move together: a value is taken only when every lane's words are complete
     if (q == 15) {
@@ -506,12 +539,15 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
     }
     __syncthreads();
     const uint2 base0 = s_excl[g];
-    const uint2 base = make_uint2(add_bytes(base0.x, gp.x), add_bytes(base0.y, gp.y));
+    // the running code before this group's first token, as c + 64 (|c| <= 16 keeps every byte
+    // in range, so later steps add whole dwords without carries between bytes)
+    uint2 run = make_uint2(add_bytes(base0.x, gp.x), add_bytes(base0.y, gp.y));
+    run = make_uint2((run.x ^ 0x80808080u) - 0x40404040u, (run.y ^ 0x80808080u) - 0x40404040u);
     // 4. reconstruct every token of this lane group; the next token's rotary rows are requested
     //    before the current token is computed
     const size_t row_off = chain * (size_t)n_keep * kHeadDim;
     const uint16_t *sl = reinterpret_cast<const uint16_t *>(s_scale);
-    const int jend = min(n_keep, j0 + kCodecRun);
+    const int jend = min(n_keep, j0 + kDecRun);
     float cn[8], sn[8];
     if (IS_KEY && j0 < jend) {
         const size_t p = (size_t)s_pos[j0 - t0] * 64 + 8 * (g & 7);
@@ -519,7 +555,7 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
         load_f32x8(a.rope_sin + p, sn);
     }
 #pragma unroll
-    for (int i = 0; i < kCodecRun; i++) {
+    for (int i = 0; i < kDecRun; i++) {
         const int j = j0 + i;
         if (j < jend) {
             float cr[8], sr[8];
@@ -532,13 +568,17 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
                     load_f32x8(a.rope_sin + p, sn);
                 }
             }
-            const uint2 c = make_uint2(add_bytes(base.x, run[i].x), add_bytes(base.y, run[i].y));
-            decode_store<IS_KEY>(a, row_off, j, g, c, sl[(j - t0) * kGroups + g], cr, sr);
+            // (c + 64) + (d + 128) - 128 per byte, d two's complement with |d| <= 32: every
+            // byte stays within [16, 240], so one 32-bit add3 is the byte-wise sum
+            const uint2 d = sd[(j - t0) * 16];
+            run = make_uint2(run.x + (d.x ^ 0x80808080u) + 0x7f7f7f80u,
+                             run.y + (d.y ^ 0x80808080u) + 0x7f7f7f80u);
+            decode_store<IS_KEY>(a, row_off, j, g, run, sl[(j - t0) * kGroups + g], cr, sr);
         }
     }
 }
 
-// grid: Lc * 2 * H * tiles_per_chain blocks; the logical tile comes from the ticket, ordered
+// grid: Lc * 2 * H * dec_tiles_per_chain blocks; the logical tile comes from the ticket, ordered
 // tile-major over the chains: tile k of a chain holds ticket k * chains + chain, so its
 // predecessor started `chains` tickets earlier and has usually published its inclusive prefix
 // by the time it is looked up (a chain-major order would start a chain's tiles together and
@@ -549,17 +589,18 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode(CodecArgs a)
     if (threadIdx.x == 0) s_ticket = (int)atomicAdd(&a.lb_ticket[0], 1u);
     __syncthreads();
     const int ticket = s_ticket;
-    const int chains = (int)(gridDim.x / (uint32_t)a.tiles_per_chain);
+    const int chains = (int)(gridDim.x / (uint32_t)a.dec_tiles_per_chain);
     const int tile = ticket / chains;
     uint32_t r = ticket % chains;
     const int h = r % a.H;
     r /= a.H;
     const int tensor = r & 1;
     const int lc = r >> 1;
+    __shared__ DecodeShared sh;
     if (tensor == 0)
-        decode_tile<true>(a, lc, h, tile, ticket, chains);
+        decode_tile<true>(a, lc, h, tile, ticket, chains, sh);
     else
-        decode_tile<false>(a, lc, h, tile, ticket, chains);
+        decode_tile<false>(a, lc, h, tile, ticket, chains, sh);
 }
 
 }  // namespace nq

@@ -127,30 +127,91 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
                                                         int W, int n_keep,
                                                         int32_t *__restrict__ positions)
 {
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t s_wave[kSelThreads / 64];
+    constexpr int kWaves = kSelThreads / 64;
+    __shared__ uint32_t hist[kWaves][256];                // one histogram per wave
+    __shared__ uint32_t s_wave[kWaves];
+    __shared__ uint64_t s_min[kWaves], s_max[kWaves];
     __shared__ uint64_t s_prefix, s_mask;
-    __shared__ int s_krem, s_all;
+    __shared__ int s_krem, s_all, s_bits;
     const int lc = blockIdx.x;
     const double *s = scores + (size_t)lc * T;
     int32_t *out = positions + (size_t)lc * n_keep;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c_end = T - W;
     const int n_cand = c_end > 1 ? c_end - 1 : 0;
     const int m = n_keep - (T - n_cand);
     const bool partial = m > 0 && m < n_cand;
 
-    if (tid == 0) { s_prefix = 0ull; s_mask = 0ull; s_krem = m; s_all = 0; }
+    if (tid == 0) { s_prefix = 0ull; s_mask = 0ull; s_krem = m; s_all = 0; s_bits = 64; }
+    if (partial) {
+        // bits shared by every candidate key (the common prefix of the smallest and largest
+        // key) need no radix pass: random scores share sign and high exponent bits, which
+        // would otherwise send every key to one histogram bucket
+        uint64_t kmin = ~0ull, kmax = 0ull;
+        for (int t0 = 1 + tid; t0 < c_end; t0 += 8 * kSelThreads) {
+            double v[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int t = t0 + u * kSelThreads;
+                v[u] = t < c_end ? s[t] : 0.0;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                if (t0 + u * kSelThreads < c_end) {
+                    const uint64_t k = order_key(v[u]);
+                    kmin = k < kmin ? k : kmin;
+                    kmax = k > kmax ? k : kmax;
+                }
+            }
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint64_t a = __shfl_xor(kmin, d), b = __shfl_xor(kmax, d);
+            kmin = a < kmin ? a : kmin;
+            kmax = b > kmax ? b : kmax;
+        }
+        if (lane == 0) { s_min[wave] = kmin; s_max[wave] = kmax; }
+        __syncthreads();
+        if (tid == 0) {
+            uint64_t lo = s_min[0], hi = s_max[0];
+            for (int w = 1; w < kWaves; w++) {
+                lo = s_min[w] < lo ? s_min[w] : lo;
+                hi = s_max[w] > hi ? s_max[w] : hi;
+            }
+            const int common = lo == hi ? 64 : __clzll((long long)(lo ^ hi));
+            s_bits = 64 - common;                           // bits left to resolve
+            s_mask = common == 64 ? ~0ull : (common == 0 ? 0ull : ~0ull << (64 - common));
+            s_prefix = lo & s_mask;
+        }
+    }
     __syncthreads();
     if (partial) {
-        for (int pass = 0; pass < 8; pass++) {
-            const int shift = 56 - 8 * pass;
-            if (tid < 256) hist[tid] = 0u;
+        for (int top = s_bits; top > 0; top -= 8) {
+            const int shift = top >= 8 ? top - 8 : 0;
+            const uint32_t dmask = top >= 8 ? 255u : ((1u << top) - 1u);
+            for (int i = tid; i < kWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
             __syncthreads();
             const uint64_t prefix = s_prefix, mask = s_mask;
-            for (int t = 1 + tid; t < c_end; t += kSelThreads) {
-                const uint64_t k = order_key(s[t]);
-                if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+            // 8 independent loads in flight per thread, then their histogram updates
+            for (int t0 = 1 + tid; t0 < c_end; t0 += 8 * kSelThreads) {
+                double v[8];
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const int t = t0 + u * kSelThreads;
+                    v[u] = t < c_end ? s[t] : 0.0;
+                }
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const uint64_t k = order_key(v[u]);
+                    if (t0 + u * kSelThreads < c_end && (k & mask) == prefix)
+                        atomicAdd(&hist[wave][(uint32_t)(k >> shift) & dmask], 1u);
+                }
+            }
+            __syncthreads();
+            if (tid < 256) {
+                uint32_t c = 0;
+                for (int w = 0; w < kWaves; w++) c += hist[w][tid];
+                hist[0][tid] = c;
             }
             __syncthreads();
             if (tid < 64) {
@@ -159,7 +220,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
                 const int krem = s_krem;
                 uint32_t c[4], loc = 0;
 #pragma unroll
-                for (int i = 0; i < 4; i++) { c[i] = hist[255 - 4 * tid - i]; loc += c[i]; }
+                for (int i = 0; i < 4; i++) { c[i] = hist[0][255 - 4 * tid - i]; loc += c[i]; }
                 uint32_t incl = loc;
 #pragma unroll
                 for (int d = 1; d < 64; d <<= 1) {
@@ -172,7 +233,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
                         if (above + c[i] >= (uint32_t)krem) {
                             const uint32_t dgt = 255 - 4 * tid - i;
                             s_prefix = prefix | ((uint64_t)dgt << shift);
-                            s_mask = mask | (255ull << shift);
+                            s_mask = mask | ((uint64_t)dmask << shift);
                             s_krem = krem - (int)above;
                             if (c[i] == (uint32_t)(krem - (int)above)) s_all = 1;
                             break;
@@ -194,6 +255,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
         const int tb = t0 + 4 * tid;
         uint32_t keepf = 0, eqf = 0;
         uint32_t gt4 = 0;
+        double v[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int t = tb + i;
+            v[i] = (partial && t >= 1 && t < c_end) ? s[t] : 0.0;
+        }
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int t = tb + i;
@@ -201,7 +268,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
             const bool cand = t >= 1 && t < c_end;
             if (!cand) { keepf |= 1u << i; continue; }
             if (!partial) { if (m > 0) keepf |= 1u << i; continue; }
-            const uint64_t k = order_key(s[t]) & mask;
+            const uint64_t k = order_key(v[i]) & mask;
             if (k > prefix) gt4 |= 1u << i;
             else if (k == prefix) eqf |= 1u << i;
         }
