@@ -140,24 +140,38 @@ __device__ __forceinline__ uint32_t f16_ceil_bits(float v)
 //                   the coordinate of smallest a moves to the other neighbouring half-integer.
 // The nearer coset wins (D8 on ties). Arg-max/min pack the index into the 3 low bits of |e|,
 // which can only matter between coordinates whose errors differ by a few ulps (a near-tie).
+// Byte work: B0 = 2f + 64 per coordinate; N = [e < 0] per byte (gathered sign bytes); the
+// D8 + 1/2 codes are 2 floor(u) + 65 = B0 + 1 - 2N; parities come from byte sums/popcounts.
 __device__ __forceinline__ void e8_nearest_code(const float u[8], uint32_t &w0, uint32_t &w1)
 {
-    float f[8], e[8];
-    uint32_t kmax = 0u, kmin = 0xffffffffu, sx = 0u;
-    float sf = 0.0f, Sa = 0.0f;
+    float e[8];
+    uint32_t kmax = 0u, kmin = 0xffffffffu, b0 = 0u, b1 = 0u;
+    float Sa = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        f[i] = __builtin_rintf(u[i]);
-        e[i] = u[i] - f[i];
+        const float f = __builtin_rintf(u[i]);
+        e[i] = u[i] - f;
         const uint32_t eb = __float_as_uint(e[i]);
-        kmax = max(kmax, (eb & 0x7ffffff8u) | (7u - (uint32_t)i));
-        kmin = min(kmin, (eb & 0x7ffffff8u) | (uint32_t)i);
-        sx ^= eb;
-        sf += f[i];
+        // (|e| with its 3 low bits replaced by the index): (eb & 0x7ffffff8) | idx
+        const uint32_t khi = (uint32_t)__builtin_amdgcn_bitop3_b32(eb, 0x7ffffff8u, 7u - (uint32_t)i, 0xEA);
+        const uint32_t klo = (uint32_t)__builtin_amdgcn_bitop3_b32(eb, 0x7ffffff8u, (uint32_t)i, 0xEA);
+        kmax = kmax > khi ? kmax : khi;
+        kmin = kmin < klo ? kmin : klo;
         Sa += __builtin_fabsf(e[i]);
+        const float t = __builtin_fmaf(2.0f, f, 64.0f);
+        if (i < 4) b0 = __builtin_amdgcn_cvt_pk_u8_f32(t, i, b0);
+        else b1 = __builtin_amdgcn_cvt_pk_u8_f32(t, i - 4, b1);
     }
-    const int P0 = ((int)sf) & 1;
-    const int P1 = P0 ^ (int)(sx >> 31);
+    // sign bytes of e (byte 3 of each float) gathered into two dwords, then [e < 0] per byte
+    const uint32_t g0 = __builtin_amdgcn_perm(__float_as_uint(e[1]), __float_as_uint(e[0]), 0x0c0c0703u) |
+                        __builtin_amdgcn_perm(__float_as_uint(e[3]), __float_as_uint(e[2]), 0x07030c0cu);
+    const uint32_t g1 = __builtin_amdgcn_perm(__float_as_uint(e[5]), __float_as_uint(e[4]), 0x0c0c0703u) |
+                        __builtin_amdgcn_perm(__float_as_uint(e[7]), __float_as_uint(e[6]), 0x07030c0cu);
+    const uint32_t n0 = (g0 >> 7) & 0x01010101u, n1 = (g1 >> 7) & 0x01010101u;
+    // sum of bytes = 2 sum(f) + 512: bit 1 is the parity of sum(f)
+    const uint32_t sb = __builtin_amdgcn_udot4(b0, 0x01010101u, __builtin_amdgcn_udot4(b1, 0x01010101u, 0u, false), false);
+    const int P0 = (int)((sb >> 1) & 1u);
+    const int P1 = P0 ^ (int)((__popc(n0) + __popc(n1)) & 1u);
     const float amax = __uint_as_float(kmax & ~7u);
     const float amin = __uint_as_float(kmin & ~7u);
     // d1 - d0 = (2 - sum a + [P1] 2 min a) - [P0] (1 - 2 max a); sum(a^2) cancels
@@ -167,27 +181,14 @@ __device__ __forceinline__ void e8_nearest_code(const float u[8], uint32_t &w0, 
     const bool half = dd < 0.0f;
     const int jf = half ? (int)(kmin & 7u) : (int)(7u - (kmax & 7u));
     const int par = half ? P1 : P0;
-    // e at index jf (select tree)
-    const float e01 = (jf & 1) ? e[1] : e[0];
-    const float e23 = (jf & 1) ? e[3] : e[2];
-    const float e45 = (jf & 1) ? e[5] : e[4];
-    const float e67 = (jf & 1) ? e[7] : e[6];
-    const float e03 = (jf & 2) ? e23 : e01;
-    const float e47 = (jf & 2) ? e67 : e45;
-    const float ej = (jf & 4) ? e47 : e03;
-    const float hs = half ? 1.0f : 0.0f;
-    uint32_t b0 = 0u, b1 = 0u;
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-        b0 = __builtin_amdgcn_cvt_pk_u8_f32(
-            __builtin_fmaf(2.0f, f[i], 64.0f + __builtin_copysignf(hs, e[i])), i, b0);
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-        b1 = __builtin_amdgcn_cvt_pk_u8_f32(
-            __builtin_fmaf(2.0f, f[i + 4], 64.0f + __builtin_copysignf(hs, e[i + 4])), i, b1);
+    if (half) {
+        b0 = b0 - 2u * n0 + 0x01010101u;   // per byte 2f + 64 - 2[e<0] + 1, never out of [0,255]
+        b1 = b1 - 2u * n1 + 0x01010101u;
+    }
     if (par) {
         // D8: re-round toward u (+2 sign(e)); D8 + 1/2: move away from u (-2 sign(e))
-        int d = (ej < 0.0f) ? -2 : 2;
+        const uint32_t neg = ((jf < 4 ? n0 : n1) >> (8 * (jf & 3))) & 1u;
+        int d = neg ? -2 : 2;
         if (half) d = -d;
         const uint32_t add = (uint32_t)d << (8 * (jf & 3));
         if (jf < 4) b0 += add; else b1 += add;
