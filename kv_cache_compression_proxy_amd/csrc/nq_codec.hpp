@@ -207,7 +207,7 @@ __device__ __forceinline__ uint2 encode_token(const CodecArgs &a, const uint16_t
     int p = pos[j];
     p = min(max(p, 0), a.T - 1);
     float x[8];
-    load_f16x8(X + (size_t)p * kHeadDim, x);
+    load_f16x8_stream(X + (size_t)p * kHeadDim, x);   // each K/V row is read once
     if (IS_KEY) {
         // RoPE removal, split-half pairs (i, i + 64) = lanes (g, g ^ 8):
         // x_i = a*C + b*S, x_{i+64} = b*C - a*S with (a, b) = (k_i, k_{i+64}).
@@ -421,18 +421,23 @@ __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off,
         float *dst = (float *)(IS_KEY ? a.out_k : a.out_v) + o;
 #pragma unroll
         for (int k = 0; k < 8; k++) x[k] = __uint_as_float(__float_as_uint(x[k]) ^ sbit);
-        *reinterpret_cast<float4 *>(dst) = make_float4(x[0], x[1], x[2], x[3]);
-        *reinterpret_cast<float4 *>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+        const u32x4 v0 = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                          __float_as_uint(x[3])};
+        const u32x4 v1 = {__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]),
+                          __float_as_uint(x[7])};
+        // the output is far larger than the caches: stream it past them
+        __builtin_nontemporal_store(v0, reinterpret_cast<u32x4 *>(dst));
+        __builtin_nontemporal_store(v1, reinterpret_cast<u32x4 *>(dst + 4));
     } else {
         // rounding to fp16 commutes with the sign, which is flipped on the packed halves
         uint16_t *dst = (uint16_t *)(IS_KEY ? a.out_k : a.out_v) + o;
         const uint32_t s2 = sbit | (sbit >> 16);
-        uint4 v;
+        u32x4 v;
         v.x = ((uint32_t)f2h_bits(x[0]) | ((uint32_t)f2h_bits(x[1]) << 16)) ^ s2;
         v.y = ((uint32_t)f2h_bits(x[2]) | ((uint32_t)f2h_bits(x[3]) << 16)) ^ s2;
         v.z = ((uint32_t)f2h_bits(x[4]) | ((uint32_t)f2h_bits(x[5]) << 16)) ^ s2;
         v.w = ((uint32_t)f2h_bits(x[6]) | ((uint32_t)f2h_bits(x[7]) << 16)) ^ s2;
-        *reinterpret_cast<uint4 *>(dst) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
     }
 }
 

@@ -25,10 +25,24 @@ __device__ __forceinline__ uint16_t f2h_bits(float x)   // round to nearest even
     return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // 8 fp16 values (one 16-byte load) -> fp32
 __device__ __forceinline__ void load_f16x8(const uint16_t *__restrict__ p, float x[8])
 {
     const uint4 v = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        x[2 * k] = h2f(w[k] & 0xffffu);
+        x[2 * k + 1] = h2f(w[k] >> 16);
+    }
+}
+
+// the same for data read once: a non-temporal load does not keep the line in the caches
+__device__ __forceinline__ void load_f16x8_stream(const uint16_t *__restrict__ p, float x[8])
+{
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int k = 0; k < 4; k++) {

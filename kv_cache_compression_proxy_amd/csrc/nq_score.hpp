@@ -49,8 +49,9 @@ __global__ __launch_bounds__(256) void k_scores(const uint16_t *__restrict__ K,
                                                 int W, int layer_begin, int tiles,
                                                 double *__restrict__ scores)
 {
-    const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
-    const int lc = id / tiles, tile = id % tiles;
+    // (no XCD-aware order here: nothing is shared between blocks, and plain order measured
+    // faster)
+    const int lc = blockIdx.x / tiles, tile = blockIdx.x % tiles;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane & 15, r4 = lane >> 4;
     const int c_end = T - W;                        // candidates: [1, c_end)
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(256) void k_scores(const uint16_t *__restrict__ K,
         for (int u = 0; u < 4; u++) {
             if (ok[u]) {
                 float x[8];
-                load_f16x8(Kh + (size_t)t[u] * kHeadDim, x);
+                load_f16x8_stream(Kh + (size_t)t[u] * kHeadDim, x);
 #pragma unroll
                 for (int k = 0; k < 8; k++) acc[u] = __builtin_fma(q[k], (double)x[k], acc[u]);
             }
