@@ -44,10 +44,110 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device copy of this many MiB (a known-size "
                          "kernel that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
-    ap.add_argument("--traffic", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                                      "profiles", "traffic.json"),
-                    help="measured HBM bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--traffic", default=None, metavar="MD",
+                    help="HBM-traffic summary to read (default: profiles/hbm_traffic_<workload>.md)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the HBM-traffic summary from two rocprofv3 --pmc runs of this "
+                         "script (FETCH_SIZE, then WRITE_SIZE, both with --copy-calibration) "
+                         "and exit")
+    ap.add_argument("--pmc-command", default="",
+                    help="the profiling command, recorded in the summary")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PHASE_KERNELS = {"score_evict": ("k_window_sum", "k_scores", "k_select"),
+                 "encode": ("k_encode",),
+                 "decode": ("k_decode_reset", "k_decode")}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources and the header: a traffic figure is valid only for the kernels
+    it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_compression_proxy_amd", "csrc")
+    for f in sorted(os.listdir(csrc)) + ["../../include/nq.h"]:
+        if f.endswith((".hpp", ".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(w) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{w.name}.md")
+
+
+def summarize_pmc(args, w):
+    """rocprofv3 counter CSVs -> profiles/hbm_traffic_<workload>.md. FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch) are scaled by what they read for a device copy of known size."""
+    import csv
+    from collections import defaultdict
+
+    def per_kernel(d, counter):
+        vals = defaultdict(list)
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if r["Counter_Name"] == counter:
+                name = r["Kernel_Name"].split("(")[0].replace("nq::", "")
+                vals[name].append(float(r["Counter_Value"]))
+        return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+    fetch = per_kernel(args.summarize_pmc[0], "FETCH_SIZE")
+    write = per_kernel(args.summarize_pmc[1], "WRITE_SIZE")
+    copy_bytes = args.copy_calibration << 20
+    if not copy_bytes or COPY_KERNEL not in fetch or COPY_KERNEL not in write:
+        sys.exit("--summarize-pmc needs the runs' --copy-calibration size and its copy kernel")
+    fk = copy_bytes / (fetch[COPY_KERNEL][0] * 1024)
+    wk = copy_bytes / (write[COPY_KERNEL][0] * 1024)
+    lines = [f"# HBM traffic per launch: {w.name}", "",
+             "rocprofv3 counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the "
+             "run's dispatches), each in a run of its own, scaled by what the same counter reads "
+             f"for a plain device copy of {args.copy_calibration} MiB ({COPY_KERNEL}: reads and "
+             "writes exactly that many bytes).", "",
+             "Commands (from /tmp with TMPDIR=/tmp; `$REPO` is the repository root):", "", "```",
+             args.pmc_command or "(not recorded)", "```", "",
+             f"Calibration: FETCH_SIZE x {fk:.4f}, WRITE_SIZE x {wk:.4f} "
+             f"(copy read {fetch[COPY_KERNEL][0]:.0f} KiB, wrote {write[COPY_KERNEL][0]:.0f} KiB "
+             f"for {copy_bytes >> 10} KiB)", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | written GB |",
+             "|---|---|---|---|---|---|"]
+    for k in sorted(set(fetch) | set(write)):
+        if k == COPY_KERNEL:
+            continue
+        f, n = fetch.get(k, (0.0, 0))
+        wr = write.get(k, (0.0, 0))[0]
+        lines.append(f"| {k} | {n} | {f:.0f} | {wr:.0f} | {f * 1024 * fk / 1e9:.4f} | "
+                     f"{wr * 1024 * wk / 1e9:.4f} |")
+    lines += ["", "Per launch of each phase (bytes; the figures bench.py reports as `traffic`):",
+              "", "```"]
+    for ph, ks in PHASE_KERNELS.items():
+        tot = sum(fetch.get(k, (0.0, 0))[0] * 1024 * fk + write.get(k, (0.0, 0))[0] * 1024 * wk
+                  for k in ks)
+        lines.append(f"traffic {ph} {int(round(tot))}")
+    lines += [f"kernel-sources {kernel_source_hash()}", "```", ""]
+    out = traffic_path(w)
+    open(out, "w").write("\n".join(lines))
+    log(f"[bench] wrote {out}")
+
+
+def read_traffic(path, phase):
+    """Bytes per launch of a phase from a traffic summary, or None when absent or when the
+    kernels have changed since the counters were taken."""
+    try:
+        txt = open(path).read().split("\n")
+    except OSError:
+        return None
+    kv = {}
+    for ln in txt:
+        parts = ln.split()
+        if len(parts) == 3 and parts[0] == "traffic":
+            kv[parts[1]] = int(parts[2])
+        elif len(parts) == 2 and parts[0] == "kernel-sources":
+            kv["_hash"] = parts[1]
+    if kv.get("_hash") != kernel_source_hash():
+        return None
+    return kv.get(phase)
 
 
 def algorithmic_bytes(w, n_keep):
@@ -105,11 +205,14 @@ def main():
               f"--gpus {args.gpus}). The hot path shards by layer with no communication; run "
               f"with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    import kvsynth
+    w = kvsynth.workload(args.workload)
+    if args.summarize_pmc:
+        summarize_pmc(args, w)
+        return
     import torch
     import kv_cache_compression_proxy_amd as nq
-    import kvsynth
 
-    w = kvsynth.workload(args.workload)
     p = nq.make_params(w.layers, w.kv_heads, w.tokens, w.window, w.evict_permille, w.bits_k,
                        w.bits_v, w.rope_base, w.layer_begin, w.layer_end)
     Lc, H, T = w.compressed_layers, w.kv_heads, w.tokens
@@ -195,20 +298,11 @@ def main():
     value = (kv_enc + kv_dec) / (ms_step * 1e-3) / 1e9
     alg = algorithmic_bytes(w, n_keep)
     dom = max(phase, key=phase.get)
-    kernel_of = {"score_evict": "k_window_sum+k_scores+k_select", "encode": "k_encode",
-                 "decode": "k_decode_reset+k_decode"}
     achieved = alg[dom] / (phase[dom] * 1e-3) / 1e9
-    traffic = None
-    try:
-        tr = json.load(open(args.traffic))
-        ent = tr.get(w.name, {}).get(dom)
-        if ent:
-            traffic = ent["bytes_per_launch"]
-    except (OSError, ValueError):
-        pass
+    traffic = read_traffic(args.traffic or traffic_path(w), dom)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": kernel_of[dom], "algorithmic_bytes_per_launch": alg[dom],
+                "kernel": "+".join(PHASE_KERNELS[dom]), "algorithmic_bytes_per_launch": alg[dom],
                 "avg_launch_ms": round(phase[dom], 4)}
     out = {
         "metric": "encode/decode fp16-KV GB/s on 1 MI355X; % of HBM peak",

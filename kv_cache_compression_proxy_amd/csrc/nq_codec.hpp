@@ -19,6 +19,7 @@ namespace nq {
 constexpr int kCodecThreads = 256;
 constexpr int kCodecRun = 16;                          // encode: tokens walked per lane group
 constexpr int kCodecTile = 16 * kCodecRun;             // encode: tokens per workgroup tile
+static_assert(kCodecTile == kCodecThreads, "encode stages one position per thread");
 constexpr int kDecRun = 8;                             // decode: tokens per lane group
 constexpr int kDecTile = 16 * kDecRun;                 // decode: tokens per workgroup tile
 
@@ -58,16 +59,24 @@ __global__ __launch_bounds__(256) void k_rope_table(RopeTheta th, int T, float *
     S[idx] = (float)sv;
 }
 
-// Hadamard butterflies of a row held as 8 values per lane (dims 8g + j), in the order h = 1, 2,
-// 4 (inside the lane) then 8, 16, 32, 64 (lane partners g^1, g^2, g^4, g^8); pair (a, b) ->
-// (a + b, a - b). The normalisation by 1/sqrt(128) is left to the caller.
+// Which 8-dim group of a 128-dim row a lane holds: lane l of a 16-lane row holds dims
+// 8 * lane_group(l) + j. The order (0 1 2 3 7 6 5 4 8 9 10 11 15 14 13 12) makes every
+// butterfly partner one DPP step away: groups G and G ^ 1, G ^ 2, G ^ 4, G ^ 8 sit in lanes
+// l ^ 1, l ^ 2, l ^ 7, l ^ 8 (quad_perm, quad_perm, row_half_mirror, row_ror:8). Loads and
+// stores of a row still cover it whole with 16 lanes, so they stay coalesced.
+__device__ __forceinline__ int lane_group(int l) { return l ^ ((l & 4) ? 3 : 0); }
+
+// Hadamard butterflies of a row held as 8 values per lane (dims 8g + j, g = lane_group of the
+// lane), in the order h = 1, 2, 4 (inside the lane) then 8, 16, 32, 64 (partner groups g ^ 1,
+// g ^ 2, g ^ 4, g ^ 8); pair (a, b) -> (a + b, a - b). The normalisation by 1/sqrt(128) is left
+// to the caller.
 //
 // Cross-lane stages keep a per-lane sign: each lane computes self + sgn * partner with one
-// fused DPP multiply-add (sgn = +1 in the lower lane of a pair, -1 in the upper one), so the
-// upper lane holds -(a - b). By induction every lane ends holding lane_sign(g) times the true
-// value, lane_sign(g) = (-1)^popcount(g); each value is one correctly rounded add or subtract
+// fused DPP multiply-add (sgn = +1 in the lower group of a pair, -1 in the upper one), so the
+// upper lane holds -(a - b). By induction every lane ends holding group_sign(g) times the true
+// value, group_sign(g) = (-1)^popcount(g); each value is one correctly rounded add or subtract
 // of the same operands as in the sequential order, so |values| match it bit for bit.
-__device__ __forceinline__ float lane_sign(int g) { return (__popc(g & 15) & 1) ? -1.0f : 1.0f; }
+__device__ __forceinline__ float group_sign(int g) { return (__popc(g & 15) & 1) ? -1.0f : 1.0f; }
 
 __device__ __forceinline__ void hadamard_butterflies(float x[8], int g)
 {
@@ -99,24 +108,7 @@ __device__ __forceinline__ void hadamard_butterflies(float x[8], int g)
 #define NQ_X8 "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7])
     asm("s_nop 1\n" NQ_FMAC_DPP("quad_perm:[1,0,3,2]") : NQ_X8 : "v"(s1));
     asm("s_nop 1\n" NQ_FMAC_DPP("quad_perm:[2,3,0,1]") : NQ_X8 : "v"(s2));
-    {
-        // lane ^ 4 = row_half_mirror (lane ^ 7) of quad_perm [3,2,1,0] (lane ^ 3)
-        float t[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) t[j] = dpp<kDppXor3>(x[j]);
-        asm("s_nop 1\n"
-            "v_fmac_f32_dpp %0, %8, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
-            "v_fmac_f32_dpp %1, %9, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
-            "v_fmac_f32_dpp %2, %10, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
-            "v_fmac_f32_dpp %3, %11, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
-            "v_fmac_f32_dpp %4, %12, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
-            "v_fmac_f32_dpp %5, %13, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
-            "v_fmac_f32_dpp %6, %14, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
-            "v_fmac_f32_dpp %7, %15, %16 row_half_mirror row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
-            : NQ_X8
-            : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(t[4]), "v"(t[5]), "v"(t[6]),
-              "v"(t[7]), "v"(s4));
-    }
+    asm("s_nop 1\n" NQ_FMAC_DPP("row_half_mirror") : NQ_X8 : "v"(s4));
     asm("s_nop 1\n" NQ_FMAC_DPP("row_ror:8") : NQ_X8 : "v"(s8));
 #undef NQ_X8
 #undef NQ_FMAC_DPP
@@ -201,13 +193,11 @@ __device__ __forceinline__ void e8_nearest_code(const float u[8], uint32_t &w0, 
 // (offset +64) and the fp16 scale bits of this lane's group.
 template <bool IS_KEY>
 __device__ __forceinline__ uint2 encode_token(const CodecArgs &a, const uint16_t *__restrict__ X,
-                                              const int32_t *__restrict__ pos, int j, int g,
-                                              float rho, float rho_inv, uint32_t &s16)
+                                              int p, int g, float rho, float rho_inv,
+                                              uint32_t &s16)
 {
-    int p = pos[j];
-    p = min(max(p, 0), a.T - 1);
     float x[8];
-    load_f16x8_stream(X + (size_t)p * kHeadDim, x);   // each K/V row is read once
+    load_f16x8_stream(X + (uint32_t)p * kHeadDim, x);   // each K/V row is read once
     if (IS_KEY) {
         // RoPE removal, split-half pairs (i, i + 64) = lanes (g, g ^ 8):
         // x_i = a*C + b*S, x_{i+64} = b*C - a*S with (a, b) = (k_i, k_{i+64}).
@@ -229,28 +219,24 @@ __device__ __forceinline__ uint2 encode_token(const CodecArgs &a, const uint16_t
     // the normalised row is x * fp32(1/sqrt(128)); rounding is monotone, so the group's
     // largest normalised magnitude is the rounded product of the largest raw one
     amax = amax * kInvSqrt128;
+    // amax / rho correctly rounded: q = amax * (1/rho), then one remainder correction
+    // (Markstein: with 1/rho rounded to nearest and q within an ulp, the corrected quotient is
+    // the correctly rounded one). amax = 0 gives s = 0.
+    const float q0 = amax * rho_inv;
+    const float rem = __builtin_fmaf(-q0, rho, amax);
+    s16 = f16_ceil_bits(__builtin_fmaf(rem, rho_inv, q0));
+    // u = x / s up to a few ulps (x * (c * rcp(s)) instead of (x * c) / s): only a point
+    // within ~1e-6 of a Voronoi facet can change lattice point, and such points are ties
+    // (the butterflies leave group_sign(g) times the row in x; the factor restores the sign).
+    // A zero scale means an all-zero group: factor 0 keeps u = 0 (rcp(0) would make NaNs).
+    const float r = __builtin_amdgcn_rcpf(h2f(s16));
+    const float f = s16 ? (kInvSqrt128 * group_sign(g)) * r : 0.0f;
     float u[8];
-    if (amax == 0.0f) {
-        s16 = 0u;
 #pragma unroll
-        for (int k = 0; k < 8; k++) u[k] = 0.0f;
-    } else {
-        // amax / rho correctly rounded: q = amax * (1/rho), then one remainder correction
-        // (Markstein: with 1/rho rounded to nearest and q within an ulp, the corrected
-        // quotient is the correctly rounded one)
-        const float q0 = amax * rho_inv;
-        const float rem = __builtin_fmaf(-q0, rho, amax);
-        s16 = f16_ceil_bits(__builtin_fmaf(rem, rho_inv, q0));
-        // u = x / s up to a few ulps (x * (c * rcp(s)) instead of (x * c) / s): only a point
-        // within ~1e-6 of a Voronoi facet can change lattice point, and such points are ties
-        // (the butterflies leave lane_sign(g) times the row in x; the factor restores the sign)
-        const float f = (kInvSqrt128 * lane_sign(g)) * __builtin_amdgcn_rcpf(h2f(s16));
+    for (int k = 0; k < 8; k++) u[k] = x[k] * f;
+    if (s16 == 0x7bffu) {   // saturated scale: |x / s| may exceed rho
 #pragma unroll
-        for (int k = 0; k < 8; k++) u[k] = x[k] * f;
-        if (s16 == 0x7bffu) {   // saturated scale: |x / s| may exceed rho
-#pragma unroll
-            for (int k = 0; k < 8; k++) u[k] = fminf(fmaxf(u[k], -rho), rho);
-        }
+        for (int k = 0; k < 8; k++) u[k] = fminf(fmaxf(u[k], -rho), rho);
     }
     uint2 c;
     e8_nearest_code(u, c.x, c.y);
@@ -268,6 +254,7 @@ __device__ __forceinline__ uint2 delta_code(uint2 cur, uint2 prev)
 struct EncodeShared {
     uint2 last[17][16];                         // predecessor codes of each lane group
     uint4 scales[kCodecTile * kGroups * 2 / 16];   // the tile's fp16 scales, stored coalesced
+    int32_t pos[kCodecTile + 1];                // positions of the tile and its predecessor
 };
 
 template <bool IS_KEY>
@@ -276,25 +263,34 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
     auto &s_last = sh.last;
     uint16_t *s_sc = reinterpret_cast<uint16_t *>(sh.scales);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane & 15, q = wave * 4 + (lane >> 4);
+    const int g = lane_group(lane & 15), q = wave * 4 + (lane >> 4);
     const int n_keep = a.n_keep;
     const size_t chain = (size_t)lc * a.H + h;
     const uint16_t *X = (IS_KEY ? a.K : a.V) +
                         ((size_t)(a.layer_begin + lc) * a.H + h) * (size_t)a.T * kHeadDim + 8 * g;
-    const int32_t *pos = a.positions + (size_t)lc * n_keep;
     int8_t *codes = (IS_KEY ? a.codes_k : a.codes_v) + chain * (size_t)n_keep * kHeadDim + 8 * g;
     const int t0 = tile * kCodecTile;
     const float rho = IS_KEY ? a.rho_k : a.rho_v;
     const float rho_inv = IS_KEY ? a.rho_inv_k : a.rho_inv_v;
     const uint2 zero = make_uint2(0x40404040u, 0x40404040u);   // code 0 in offset form
 
+    // positions of tokens t0 - 1 .. t0 + kCodecTile - 1 (clamped into the cache) to LDS
+    {
+        const int32_t *pos = a.positions + (size_t)lc * n_keep;
+        const int jj = t0 - 1 + (int)threadIdx.x;
+        if (jj >= 0 && jj < n_keep) sh.pos[threadIdx.x] = min(max(pos[jj], 0), a.T - 1);
+        if (threadIdx.x == 0 && t0 + kCodecTile - 1 < n_keep)
+            sh.pos[kCodecTile] = min(max(pos[t0 + kCodecTile - 1], 0), a.T - 1);
+    }
+    __syncthreads();
+    const int32_t *s_pos = sh.pos + 1;   // s_pos[j - t0]
+
     // the tile's predecessor token, coded (not stored) by lane group 0
     if (q == 0) {
         uint2 hc = zero;
-        const int jh = tile * kCodecTile - 1;
-        if (jh >= 0) {
+        if (t0 > 0) {
             uint32_t s16;
-            hc = encode_token<IS_KEY>(a, X, pos, jh, g, rho, rho_inv, s16);
+            hc = encode_token<IS_KEY>(a, X, s_pos[-1], g, rho, rho_inv, s16);
         }
         s_last[0][g] = hc;
     }
@@ -304,7 +300,7 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
         const int j = j0 + i;
         if (j < n_keep) {
             uint32_t s16;
-            const uint2 c = encode_token<IS_KEY>(a, X, pos, j, g, rho, rho_inv, s16);
+            const uint2 c = encode_token<IS_KEY>(a, X, s_pos[j - t0], g, rho, rho_inv, s16);
             s_sc[(j - t0) * kGroups + g] = (uint16_t)s16;
             if (i == 0)
                 first = c;
@@ -406,7 +402,7 @@ __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off,
     x[5] = __builtin_fmaf(hs, (float)((ub1 >> 8) & 0xffu), off);
     x[6] = __builtin_fmaf(hs, (float)((ub1 >> 16) & 0xffu), off);
     x[7] = __builtin_fmaf(hs, (float)((ub1 >> 24) & 0xffu), off);
-    hadamard_butterflies(x, g);   // x = lane_sign(g) * (the reconstructed row)
+    hadamard_butterflies(x, g);   // x = group_sign(g) * (the reconstructed row)
     if (IS_KEY) {
         // RoPE at the stored position: k_i = x_i*C - x_{i+64}*S, k_{i+64} = x_{i+64}*C + x_i*S.
         // The partner lane g^8 carries the opposite lane sign, hence the flipped +-.
@@ -415,7 +411,7 @@ __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off,
         for (int k = 0; k < 8; k++)
             x[k] = __builtin_fmaf(sg, lane_xor8(x[k]) * sr[k], x[k] * cr[k]);
     }
-    const uint32_t sbit = (__popc(g & 15) & 1) ? 0x80000000u : 0u;   // lane_sign as a sign bit
+    const uint32_t sbit = (__popc(g & 15) & 1) ? 0x80000000u : 0u;   // group_sign as a sign bit
     const size_t o = row_off + (size_t)j * kHeadDim + 8 * g;
     if (a.out_f32) {
         float *dst = (float *)(IS_KEY ? a.out_k : a.out_v) + o;
@@ -458,7 +454,7 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
     auto &s_pos = sh.pos;
     auto &s_scale = sh.scale;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane & 15, q = wave * 4 + (lane >> 4);
+    const int g = lane_group(lane & 15), q = wave * 4 + (lane >> 4);
     const int n_keep = a.n_keep;
     const size_t chain = (size_t)lc * a.H + h;
     const int t0 = tile * kDecTile;

@@ -59,11 +59,9 @@ __device__ __forceinline__ void load_f32x8(const float *__restrict__ p, float x[
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-// Cross-lane moves inside a 16-lane row with DPP (no LDS traffic). Control words: quad_perm
-// [1,0,3,2] = lane ^ 1, [2,3,0,1] = lane ^ 2, [3,2,1,0] = lane ^ 3, row_half_mirror = lane ^ 7
-// (low 3 bits), row_ror:8 = lane ^ 8 within the row.
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppXor3 = 0x1B, kDppHalfMirror = 0x141,
-              kDppRor8 = 0x128;
+// Cross-lane moves inside a 16-lane row with DPP (no LDS traffic): row_ror:8 = lane ^ 8
+// within the row.
+constexpr int kDppRor8 = 0x128;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
@@ -71,9 +69,6 @@ __device__ __forceinline__ float dpp(float v)
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-__device__ __forceinline__ float lane_xor1(float v) { return dpp<kDppXor1>(v); }
-__device__ __forceinline__ float lane_xor2(float v) { return dpp<kDppXor2>(v); }
-__device__ __forceinline__ float lane_xor4(float v) { return dpp<kDppHalfMirror>(dpp<kDppXor3>(v)); }
 __device__ __forceinline__ float lane_xor8(float v) { return dpp<kDppRor8>(v); }
 
 // Byte-wise (mod 256) addition of four packed bytes, no carries between bytes.
