@@ -78,7 +78,7 @@ __device__ __forceinline__ int lane_group(int l) { return l ^ ((l & 4) ? 3 : 0);
 // of the same operands as in the sequential order, so |values| match it bit for bit.
 __device__ __forceinline__ float group_sign(int g) { return (__popc(g & 15) & 1) ? -1.0f : 1.0f; }
 
-__device__ __forceinline__ void hadamard_butterflies(float x[8], int g)
+__device__ __forceinline__ void hadamard_in_lane(float x[8])
 {
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1) {
@@ -91,6 +91,10 @@ __device__ __forceinline__ void hadamard_butterflies(float x[8], int g)
             }
         }
     }
+}
+
+__device__ __forceinline__ void hadamard_cross_lane(float x[8], int g)
+{
     const float s1 = (g & 1) ? -1.0f : 1.0f, s2 = (g & 2) ? -1.0f : 1.0f;
     const float s4 = (g & 4) ? -1.0f : 1.0f, s8 = (g & 8) ? -1.0f : 1.0f;
     // x[j] += s * x[j] of the partner lane: v_fmac_f32 with a DPP-routed first operand (the
@@ -112,6 +116,12 @@ __device__ __forceinline__ void hadamard_butterflies(float x[8], int g)
     asm("s_nop 1\n" NQ_FMAC_DPP("row_ror:8") : NQ_X8 : "v"(s8));
 #undef NQ_X8
 #undef NQ_FMAC_DPP
+}
+
+__device__ __forceinline__ void hadamard_butterflies(float x[8], int g)
+{
+    hadamard_in_lane(x);
+    hadamard_cross_lane(x, g);
 }
 
 // Smallest fp16 >= v (v > 0 finite), saturating at 65504.
@@ -390,19 +400,55 @@ __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off,
                                              uint2 code, uint32_t s16, const float cr[8],
                                              const float sr[8])
 {
-    // x = s * c / 2 times the Hadamard normalisation, as fma(scale, c + 64, -64 * scale)
-    const float hs = (0.5f * kInvSqrt128) * h2f(s16), off = -64.0f * hs;
-    const uint32_t ub0 = code.x, ub1 = code.y;
+    // The in-lane butterflies (h = 1, 2, 4) run on the integer codes in packed fp16, where
+    // they are exact (|sums| <= 8 * 16): each code byte c + 64 becomes the fp16 1024 + (c + 64)
+    // by placing it under the exponent byte 0x64, and one packed add removes the 1088. One
+    // v_pk_add_f16 with op_sel / neg_hi gives a pair's sum in the low half and its difference
+    // in the high half. Then x = (s / 2) * (1 / sqrt(128)) * (sum of codes), rounded once.
+    const float hs = (0.5f * kInvSqrt128) * h2f(s16);
+    uint32_t q0 = __builtin_amdgcn_perm(0x64646464u, code.x, 0x04010400u);   // (c0, c1)
+    uint32_t q1 = __builtin_amdgcn_perm(0x64646464u, code.x, 0x04030402u);   // (c2, c3)
+    uint32_t q2 = __builtin_amdgcn_perm(0x64646464u, code.y, 0x04010400u);   // (c4, c5)
+    uint32_t q3 = __builtin_amdgcn_perm(0x64646464u, code.y, 0x04030402u);   // (c6, c7)
+    uint32_t r0, r1, r2, r3;
+    asm("v_pk_add_f16 %0, %0, %4\n"
+        "v_pk_add_f16 %1, %1, %4\n"
+        "v_pk_add_f16 %2, %2, %4\n"
+        "v_pk_add_f16 %3, %3, %4\n"
+        // h = 1: (a, b) -> (a + b, a - b) inside each register
+        "v_pk_add_f16 %0, %0, %0 op_sel:[0,1] op_sel_hi:[0,1] neg_hi:[0,1]\n"
+        "v_pk_add_f16 %1, %1, %1 op_sel:[0,1] op_sel_hi:[0,1] neg_hi:[0,1]\n"
+        "v_pk_add_f16 %2, %2, %2 op_sel:[0,1] op_sel_hi:[0,1] neg_hi:[0,1]\n"
+        "v_pk_add_f16 %3, %3, %3 op_sel:[0,1] op_sel_hi:[0,1] neg_hi:[0,1]\n"
+        : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3)
+        : "s"(0xE440E440u));   // (-1088, -1088)
+    // now q0 = (y0, y1), q1 = (y2, y3), q2 = (y4, y5), q3 = (y6, y7)
+    asm("v_pk_add_f16 %0, %4, %5 op_sel:[0,0] op_sel_hi:[0,0] neg_hi:[0,1]\n"   // (z0, z2)
+        "v_pk_add_f16 %1, %4, %5 op_sel:[1,1] op_sel_hi:[1,1] neg_hi:[0,1]\n"   // (z1, z3)
+        "v_pk_add_f16 %2, %6, %7 op_sel:[0,0] op_sel_hi:[0,0] neg_hi:[0,1]\n"   // (z4, z6)
+        "v_pk_add_f16 %3, %6, %7 op_sel:[1,1] op_sel_hi:[1,1] neg_hi:[0,1]\n"   // (z5, z7)
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(q0), "v"(q1), "v"(q2), "v"(q3));
+    asm("v_pk_add_f16 %0, %4, %6 op_sel:[0,0] op_sel_hi:[0,0] neg_hi:[0,1]\n"   // (o0, o4)
+        "v_pk_add_f16 %1, %4, %6 op_sel:[1,1] op_sel_hi:[1,1] neg_hi:[0,1]\n"   // (o2, o6)
+        "v_pk_add_f16 %2, %5, %7 op_sel:[0,0] op_sel_hi:[0,0] neg_hi:[0,1]\n"   // (o1, o5)
+        "v_pk_add_f16 %3, %5, %7 op_sel:[1,1] op_sel_hi:[1,1] neg_hi:[0,1]\n"   // (o3, o7)
+        : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3)
+        : "v"(r0), "v"(r1), "v"(r2), "v"(r3));
+    // fp16 half times fp32 scale in one v_fma_mix_f32 (product rounded once, + 0)
     float x[8];
-    x[0] = __builtin_fmaf(hs, (float)(ub0 & 0xffu), off);
-    x[1] = __builtin_fmaf(hs, (float)((ub0 >> 8) & 0xffu), off);
-    x[2] = __builtin_fmaf(hs, (float)((ub0 >> 16) & 0xffu), off);
-    x[3] = __builtin_fmaf(hs, (float)((ub0 >> 24) & 0xffu), off);
-    x[4] = __builtin_fmaf(hs, (float)(ub1 & 0xffu), off);
-    x[5] = __builtin_fmaf(hs, (float)((ub1 >> 8) & 0xffu), off);
-    x[6] = __builtin_fmaf(hs, (float)((ub1 >> 16) & 0xffu), off);
-    x[7] = __builtin_fmaf(hs, (float)((ub1 >> 24) & 0xffu), off);
-    hadamard_butterflies(x, g);   // x = group_sign(g) * (the reconstructed row)
+    asm("v_fma_mix_f32 %0, %8, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %4, %8, %12, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %2, %9, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %6, %9, %12, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %1, %10, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %5, %10, %12, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %3, %11, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %7, %11, %12, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7])
+        : "v"(q0), "v"(q1), "v"(q2), "v"(q3), "v"(hs));
+    hadamard_cross_lane(x, g);   // x = group_sign(g) * (the reconstructed row)
     if (IS_KEY) {
         // RoPE at the stored position: k_i = x_i*C - x_{i+64}*S, k_{i+64} = x_{i+64}*C + x_i*S.
         // The partner lane g^8 carries the opposite lane sign, hence the flipped +-.
@@ -429,16 +475,16 @@ __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off,
         uint16_t *dst = (uint16_t *)(IS_KEY ? a.out_k : a.out_v) + o;
         const uint32_t s2 = sbit | (sbit >> 16);
         u32x4 v;
-        v.x = ((uint32_t)f2h_bits(x[0]) | ((uint32_t)f2h_bits(x[1]) << 16)) ^ s2;
-        v.y = ((uint32_t)f2h_bits(x[2]) | ((uint32_t)f2h_bits(x[3]) << 16)) ^ s2;
-        v.z = ((uint32_t)f2h_bits(x[4]) | ((uint32_t)f2h_bits(x[5]) << 16)) ^ s2;
-        v.w = ((uint32_t)f2h_bits(x[6]) | ((uint32_t)f2h_bits(x[7]) << 16)) ^ s2;
+        v.x = f2h_pack(x[0], x[1]) ^ s2;
+        v.y = f2h_pack(x[2], x[3]) ^ s2;
+        v.z = f2h_pack(x[4], x[5]) ^ s2;
+        v.w = f2h_pack(x[6], x[7]) ^ s2;
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
     }
 }
 
 struct DecodeShared {
-    uint2 tot[16][16];                          // running-sum totals of the lane groups
+    uint2 tot[4][16];                           // running-sum totals of the waves
     uint2 excl[16];                             // the tile's exclusive prefix
     int32_t pos[kDecTile];                      // the tile's positions
     uint4 scale[kDecTile * kGroups * 2 / 16];     // the tile's fp16 scales
@@ -464,17 +510,30 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
     // 0. stage the tile's positions and scales in LDS with coalesced loads; they arrive while the
     //    running sum and the look-back below proceed
     {
-        const uint4 *sc = reinterpret_cast<const uint4 *>(
-            (IS_KEY ? a.scales_k : a.scales_v) + (chain * (size_t)n_keep + t0) * kGroups);
-        for (int c = threadIdx.x; c < 2 * nt; c += kCodecThreads) s_scale[c] = sc[c];
-        const uint4 *dc = reinterpret_cast<const uint4 *>(
+        // every load of a thread is issued before the first LDS store, so they are in flight
+        // together (one memory latency per tile, not one per chunk)
+        constexpr int kDeltaChunks = kDecTile * kHeadDim / 16 / kCodecThreads;
+        static_assert(kDecTile * kGroups * 2 / 16 <= kCodecThreads && kDecTile <= kCodecThreads,
+                      "one scale chunk and one position per thread");
+        const u32x4 *dc = reinterpret_cast<const u32x4 *>(
             (IS_KEY ? a.codes_k : a.codes_v) + (chain * (size_t)n_keep + t0) * kHeadDim);
-        for (int c = threadIdx.x; c < 8 * nt; c += kCodecThreads) sh.delta[c] = dc[c];
-        if (IS_KEY) {
-            const int32_t *pos = a.positions + (size_t)lc * n_keep + t0;
-            for (int i = threadIdx.x; i < nt; i += kCodecThreads)
-                s_pos[i] = min(max(pos[i], 0), a.T - 1);
-        }
+        const u32x4 *sc = reinterpret_cast<const u32x4 *>(
+            (IS_KEY ? a.scales_k : a.scales_v) + (chain * (size_t)n_keep + t0) * kGroups);
+        const int tid = threadIdx.x;
+        u32x4 d[kDeltaChunks], sv = {0u, 0u, 0u, 0u};
+        int pv = 0;
+#pragma unroll
+        for (int k = 0; k < kDeltaChunks; k++)
+            if (tid + k * kCodecThreads < 8 * nt)
+                d[k] = __builtin_nontemporal_load(dc + tid + k * kCodecThreads);
+        if (tid < 2 * nt) sv = __builtin_nontemporal_load(sc + tid);
+        if (IS_KEY && tid < nt) pv = a.positions[(size_t)lc * n_keep + t0 + tid];
+#pragma unroll
+        for (int k = 0; k < kDeltaChunks; k++)
+            if (tid + k * kCodecThreads < 8 * nt)
+                sh.delta[tid + k * kCodecThreads] = make_uint4(d[k].x, d[k].y, d[k].z, d[k].w);
+        if (tid < 2 * nt) s_scale[tid] = make_uint4(sv.x, sv.y, sv.z, sv.w);
+        if (IS_KEY && tid < nt) s_pos[tid] = min(max(pv, 0), a.T - 1);
     }
 
     // 1. the byte-wise sum of this lane group's deltas (from the staged tile)
@@ -489,18 +548,22 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
             acc = make_uint2(add_bytes(acc.x, d.x), add_bytes(acc.y, d.y));
         }
     }
-    // 2. prefix over the lane groups before this one (log-step scan through LDS); group 15's
-    //    lanes then hold the tile total in gp + acc
+    // 2. prefix over the lane groups before this one: across the 4 rows of a wave with lane
+    //    shuffles, then across the 4 waves through LDS (one barrier); group 15's lanes then
+    //    hold the tile total in gp + acc
+    const int row = lane >> 4;
     uint2 incl = acc;
 #pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-        s_tot[q][g] = incl;
-        __syncthreads();
-        if (q >= d) {
-            const uint2 t = s_tot[q - d][g];
-            incl = make_uint2(add_bytes(incl.x, t.x), add_bytes(incl.y, t.y));
-        }
-        __syncthreads();
+    for (int d = 1; d < 4; d <<= 1) {
+        const uint2 t = make_uint2((uint32_t)__shfl_up((int)incl.x, 16 * d),
+                                   (uint32_t)__shfl_up((int)incl.y, 16 * d));
+        if (row >= d) incl = make_uint2(add_bytes(incl.x, t.x), add_bytes(incl.y, t.y));
+    }
+    if (row == 3) s_tot[wave][g] = incl;
+    __syncthreads();
+    for (int w = 0; w < wave; w++) {
+        const uint2 t = s_tot[w][g];
+        incl = make_uint2(add_bytes(incl.x, t.x), add_bytes(incl.y, t.y));
     }
     const uint2 gp = make_uint2(sub_bytes(incl.x, acc.x), sub_bytes(incl.y, acc.y));
     // 3. decoupled look-back, done by lane group 15 (it holds the tile total); the 16 lanes of

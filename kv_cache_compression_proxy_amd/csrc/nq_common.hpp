@@ -1,9 +1,11 @@
 // Device helpers shared by the gfx950 kernels of libnq.
 //
 // Lane layout used by every row kernel: a 128-float head row is spread over 16 consecutive
-// lanes, lane g (= lane & 15) holding the 8 consecutive dims [8g, 8g+8) -- one 16-byte fp16
-// load per lane, a fully coalesced 256-byte row per lane group, and one E8 group per lane.
-// A wave64 therefore works on 4 rows at once ("lane groups" 0..3).
+// lanes, each holding one group of 8 consecutive dims -- one 16-byte fp16 load per lane, a
+// fully coalesced 256-byte row per 16 lanes, and one E8 group per lane. Lane l (= lane & 15)
+// holds group l in the scoring and attention kernels and group lane_group(l) (a fixed
+// permutation that suits the Hadamard butterflies) in the codec kernels. A wave64 therefore
+// works on 4 rows at once ("lane groups" 0..3).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,6 +28,14 @@ __device__ __forceinline__ uint16_t f2h_bits(float x)   // round to nearest even
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed fp16 pair (lo, hi), rounded to nearest even (v_cvt_pk_f16_f32)
+__device__ __forceinline__ uint32_t f2h_pack(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
 
 // 8 fp16 values (one 16-byte load) -> fp32
 __device__ __forceinline__ void load_f16x8(const uint16_t *__restrict__ p, float x[8])
