@@ -52,6 +52,10 @@ def parse():
                          "and exit")
     ap.add_argument("--pmc-command", default="",
                     help="the profiling command, recorded in the summary")
+    ap.add_argument("--decode-step", action="store_true",
+                    help="time the one-token GQA decode step over the long-context compressed "
+                         "cache instead: fused nq_decode_attend against nq_decode + "
+                         "nq_attend_decode")
     return ap.parse_args()
 
 
@@ -198,29 +202,11 @@ def cpu_baseline(w, layers: int):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
-              f"--gpus {args.gpus}). The hot path shards by layer with no communication; run "
-              f"with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-    import kvsynth
-    w = kvsynth.workload(args.workload)
-    if args.summarize_pmc:
-        summarize_pmc(args, w)
-        return
+def upload_workload(w, dev):
+    """K, V [L, H, T, 128] fp16 on the device, generated on the host a few layers at a time."""
     import torch
-    import kv_cache_compression_proxy_amd as nq
-
-    p = nq.make_params(w.layers, w.kv_heads, w.tokens, w.window, w.evict_permille, w.bits_k,
-                       w.bits_v, w.rope_base, w.layer_begin, w.layer_end)
-    Lc, H, T = w.compressed_layers, w.kv_heads, w.tokens
-    n_keep = nq.nq_keep_count(p)
-    dev = torch.device("cuda:0")
-    log(f"[bench] workload {w.name}: Lc={Lc} H={H} T={T} n_keep={n_keep}")
-
-    t0 = time.time()
+    import kvsynth
+    H, T = w.kv_heads, w.tokens
     K = torch.empty((w.layers, H, T, 128), dtype=torch.float16, device=dev)
     V = torch.empty_like(K)
     chunk = 4
@@ -236,6 +222,141 @@ def main():
         K[l0:l0 + len(ls)].copy_(torch.from_numpy(hk))
         V[l0:l0 + len(ls)].copy_(torch.from_numpy(hv))
     torch.cuda.synchronize()
+    return K, V
+
+
+def decode_step(args):
+    """One-token GQA decode step over the long-context compressed cache (32 query heads over 8
+    kv heads, one fp16 query per layer): the fused nq_decode_attend against the two-call path
+    nq_decode (fp16 K_hat/V_hat written to HBM) + nq_attend_decode (read back)."""
+    import torch
+    import kv_cache_compression_proxy_amd as nq
+    import kvsynth
+    w4 = kvsynth.workload(4)
+    w = kvsynth.workload(2)   # the cache the decode step attends over
+    p = nq.make_params(w.layers, w.kv_heads, w.tokens, w.window, w.evict_permille, w.bits_k,
+                       w.bits_v, w.rope_base, w.layer_begin, w.layer_end)
+    Lc, H, T = w.compressed_layers, w.kv_heads, w.tokens
+    n = nq.nq_keep_count(p)
+    dev = torch.device("cuda:0")
+    log(f"[decode-step] cache {w.name}: Lc={Lc} H={H} T={T} n_keep={n}, {w4.q_heads} query heads")
+    t0 = time.time()
+    K, V = upload_workload(w, dev)
+    cos, sin = nq.rope_table(p, dev)
+    positions = torch.empty((Lc, n), dtype=torch.int32, device=dev)
+    nq.nq_score_evict(p, K, positions, nq.workspace(nq.nq_score_evict_workspace_bytes(p), dev))
+    ck = torch.empty((Lc, H, n, 128), dtype=torch.int8, device=dev)
+    cv = torch.empty_like(ck)
+    sk = torch.empty((Lc, H, n, 16), dtype=torch.float16, device=dev)
+    sv = torch.empty_like(sk)
+    nq.nq_encode(p, K, V, positions, cos, sin, ck, cv, sk, sv)
+    torch.cuda.synchronize()
+    del K, V
+    torch.cuda.empty_cache()
+    log(f"[decode-step] compressed cache built in {time.time() - t0:.1f}s")
+    Hq = w4.q_heads
+    Q = torch.from_numpy(kvsynth.queries(w4)).to(dev)
+    out = torch.empty((Lc, Hq, 128), dtype=torch.float32, device=dev)
+    ws_f = nq.workspace(nq.nq_decode_attend_workspace_bytes(p, Hq), dev)
+    Ko = torch.empty((Lc, H, n, 128), dtype=torch.float16, device=dev)
+    Vo = torch.empty_like(Ko)
+    ws_d = nq.workspace(nq.nq_decode_workspace_bytes(p), dev)
+    ws_a = nq.workspace(nq.nq_attend_workspace_bytes(p, Hq, n), dev)
+    out2 = torch.empty_like(out)
+    stream = torch.cuda.current_stream()
+
+    def fused():
+        nq.nq_decode_attend(p, ck, cv, sk, sv, positions, cos, sin, Q, Hq, out, ws_f, stream)
+
+    def two_call(ev=None):
+        nq.nq_decode(p, ck, cv, sk, sv, positions, cos, sin, Ko, Vo, nq.NQ_OUT_F16, ws_d, stream)
+        if ev is not None:
+            ev.record(stream)
+        nq.nq_attend_decode(p, Q, Hq, Ko, Vo, n, out2, ws_a, stream)
+
+    def timed(fn, mid=False):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        a.record(stream)
+        for i in range(args.steps):
+            starts[i].record(stream)
+            fn(mids[i]) if mid else fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        first = sum(s.elapsed_time(m) for s, m in zip(starts, mids)) / args.steps if mid else None
+        return a.elapsed_time(b) / args.steps, first
+
+    ms_f, _ = timed(fused)
+    ms_2, ms_dec = timed(two_call, mid=True)
+    diff = (out - out2).abs().max().item() / max(Vo.float().abs().max().item(), 1e-30)
+    log(f"[decode-step] fused {ms_f:.3f} ms; two-call {ms_2:.3f} ms (decode {ms_dec:.3f}); "
+        f"max |fused - two-call| / max|v_hat| = {diff:.2e}")
+    kept = Lc * H * n
+    kv16 = kept * 2 * 256                                  # fp16 K+V the step attends over
+    alg_f = kept * (2 * 128 + 2 * 32) + Lc * n * 4 + T * 64 * 4 * 2 + Lc * Hq * (256 + 512)
+    alg_2 = kept * (2 * 128 + 2 * 32 + 2 * 256) * 1 + kept * 2 * 256 + Lc * n * 4 + T * 512
+    achieved = alg_f / (ms_f * 1e-3) / 1e9
+    res = {
+        "metric": "one-token GQA decode step over the compressed cache: fp16-KV GB/s attended",
+        "value": round(kv16 / (ms_f * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_f, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w4.name, "cache": w.name, "layers": Lc, "kv_heads": H,
+                   "q_heads": Hq, "tokens": T, "n_keep": n, "parallelism": "none (1 GPU)"},
+        "two_call_ms": round(ms_2, 4),
+        "two_call_decode_ms": round(ms_dec, 4),
+        "speedup_vs_two_call": round(ms_2 / ms_f, 3),
+        "two_call_value": round(kv16 / (ms_2 * 1e-3) / 1e9, 2),
+        "max_abs_diff_vs_two_call_rel": float(f"{diff:.3e}"),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "k_decode_reset+k_decode_attend+k_decode_attend_merge",
+                     "algorithmic_bytes_per_launch": alg_f, "avg_launch_ms": round(ms_f, 4)},
+        "two_call_algorithmic_frac_of_peak": round(alg_2 / (ms_2 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                                   4),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}). The hot path shards by layer with no communication; run "
+              f"with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import kvsynth
+    w = kvsynth.workload(args.workload)
+    if args.summarize_pmc:
+        summarize_pmc(args, w)
+        return
+    if args.decode_step:
+        decode_step(args)
+        return
+    import torch
+    import kv_cache_compression_proxy_amd as nq
+
+    p = nq.make_params(w.layers, w.kv_heads, w.tokens, w.window, w.evict_permille, w.bits_k,
+                       w.bits_v, w.rope_base, w.layer_begin, w.layer_end)
+    Lc, H, T = w.compressed_layers, w.kv_heads, w.tokens
+    n_keep = nq.nq_keep_count(p)
+    dev = torch.device("cuda:0")
+    log(f"[bench] workload {w.name}: Lc={Lc} H={H} T={T} n_keep={n_keep}")
+
+    t0 = time.time()
+    K, V = upload_workload(w, dev)
     log(f"[bench] inputs generated and uploaded in {time.time() - t0:.1f}s")
 
     if args.copy_calibration:

@@ -145,6 +145,30 @@ nq_status nq_attend_decode(const nq_params *p, const void *Q, int32_t q_heads, c
                            const void *V, int32_t n_tok, float *out, void *workspace,
                            size_t ws_bytes, void *stream);
 
+/* Device workspace needed by nq_decode_attend for q_heads query heads (bytes). 0 if p is
+ * invalid. */
+size_t nq_decode_attend_workspace_bytes(const nq_params *p, int32_t q_heads);
+
+/* One-token grouped-query attention straight from the compressed cache (the VQKV page,
+ * "推理流程集成": reconstruct on demand inside attention). Computes what nq_decode followed by
+ * nq_attend_decode over its fp32 output computes -- o_j = sum_t softmax_t(<q_j, k_t> /
+ * sqrt(128)) v_t over the n_keep kept tokens, query head j reading kv head j / (q_heads / H),
+ * k_t and v_t the reconstructions of step 7 -- without writing k_t, v_t anywhere: keys are
+ * rebuilt in registers, and the value sum is accumulated on the dequantised codes with the
+ * inverse Hadamard applied once per query head (it is linear). fp32 throughout; the result
+ * differs from the two-call path only by rounding order.
+ *   codes_k, codes_v, scales_k, scales_v, positions, rope_cos, rope_sin  as for nq_decode
+ *   Q      fp16 [L_c][q_heads][128]; q_heads a multiple of H with q_heads/H in {1, 2, 4, 8}
+ *   out    fp32 [L_c][q_heads][128] out (zeros when n_keep = 0)
+ *   workspace  nq_decode_attend_workspace_bytes(p, q_heads) bytes (look-back words and the
+ *              per-tile partials; contents on entry do not matter, calls sharing one
+ *              workspace must not overlap) */
+nq_status nq_decode_attend(const nq_params *p, const int8_t *codes_k, const int8_t *codes_v,
+                           const void *scales_k, const void *scales_v, const int32_t *positions,
+                           const float *rope_cos, const float *rope_sin, const void *Q,
+                           int32_t q_heads, float *out, void *workspace, size_t ws_bytes,
+                           void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *nq_status_string(nq_status s);
 

@@ -33,7 +33,8 @@ NQ_OK, NQ_ERR_INVALID_ARG, NQ_ERR_UNSUPPORTED, NQ_ERR_WORKSPACE, NQ_ERR_HIP = 0,
 NQ_OUT_F16, NQ_OUT_F32 = 0, 1
 EXPORTED = ("nq_keep_count", "nq_check_params", "nq_score_evict_workspace_bytes",
             "nq_decode_workspace_bytes", "nq_attend_workspace_bytes", "nq_rope_table",
-            "nq_score_evict", "nq_encode", "nq_decode", "nq_attend_decode", "nq_status_string")
+            "nq_score_evict", "nq_encode", "nq_decode", "nq_attend_decode",
+            "nq_decode_attend_workspace_bytes", "nq_decode_attend", "nq_status_string")
 
 
 class NqParams(C.Structure):
@@ -60,6 +61,9 @@ _sig = {
     "nq_decode": (C.c_int, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, C.c_int, _v, C.c_size_t, _v]),
     "nq_attend_decode": (C.c_int, [_P, _v, C.c_int32, _v, _v, C.c_int32, _v, _v, C.c_size_t,
                                    _v]),
+    "nq_decode_attend_workspace_bytes": (C.c_size_t, [_P, C.c_int32]),
+    "nq_decode_attend": (C.c_int, [_P, _v, _v, _v, _v, _v, _v, _v, _v, C.c_int32, _v, _v,
+                                   C.c_size_t, _v]),
     "nq_status_string": (C.c_char_p, [C.c_int]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -156,6 +160,19 @@ def nq_attend_decode(p, Q, q_heads, K, V, n_tok, out, workspace, stream=None):
                                                   _stream(stream)))
 
 
+def nq_decode_attend_workspace_bytes(p: NqParams, q_heads: int) -> int:
+    return _lib.nq_decode_attend_workspace_bytes(C.byref(p), q_heads)
+
+
+def nq_decode_attend(p, codes_k, codes_v, scales_k, scales_v, positions, rope_cos, rope_sin, Q,
+                     q_heads, out, workspace, stream=None):
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _ok("nq_decode_attend", _lib.nq_decode_attend(
+        C.byref(p), _ptr(codes_k), _ptr(codes_v), _ptr(scales_k), _ptr(scales_v), _ptr(positions),
+        _ptr(rope_cos), _ptr(rope_sin), _ptr(Q), q_heads, _ptr(out), _ptr(workspace), ws,
+        _stream(stream)))
+
+
 def nq_status_string(status: int) -> str:
     return _lib.nq_status_string(status).decode()
 
@@ -236,5 +253,18 @@ def attend(c_params: NqParams, Q, K_hat, V_hat, stream=None):
     return out
 
 
+def attend_compressed(c: Compressed, Q, stream=None):
+    """One-token GQA straight from the compressed cache (no K_hat/V_hat written):
+    Q fp16 [Lc, Hq, 128] -> fp32 [Lc, Hq, 128]."""
+    import torch
+    Lc, Hq, _ = Q.shape
+    out = torch.empty((Lc, Hq, 128), dtype=torch.float32, device=Q.device)
+    ws = workspace(nq_decode_attend_workspace_bytes(c.params, Hq), Q.device)
+    nq_decode_attend(c.params, c.codes_k, c.codes_v, c.scales_k, c.scales_v, c.positions,
+                     c.rope_cos, c.rope_sin, Q, Hq, out, ws, stream)
+    return out
+
+
 __all__ = ["NqParams", "NqError", "Compressed", "PRESETS", "params_for", "make_params",
-           "compress", "decompress", "attend", "rope_table", "workspace", *EXPORTED]
+           "compress", "decompress", "attend", "attend_compressed", "rope_table", "workspace",
+           *EXPORTED]

@@ -11,6 +11,7 @@
 #include "nq.h"
 #include "nq_attend.hpp"
 #include "nq_codec.hpp"
+#include "nq_fused.hpp"
 #include "nq_score.hpp"
 
 namespace {
@@ -140,6 +141,32 @@ AttWs attend_ws(const nq_params *p, int32_t q_heads, int32_t n_tok, void *base)
     w.l = (float *)((char *)base + a);
     w.acc = (float *)((char *)base + 2 * a);
     w.bytes = 2 * a + c;
+    return w;
+}
+
+struct FusedWs {
+    uint32_t *ticket, *agg, *incl;
+    float *part;
+    size_t bytes;
+    int32_t pairs, tiles;
+};
+
+FusedWs fused_ws(const nq_params *p, int32_t q_heads, void *base)
+{
+    FusedWs w;
+    w.pairs = compressed_layers(p) * p->kv_heads;
+    w.tiles = decode_tiles(p);
+    const size_t G = (size_t)(q_heads / p->kv_heads);
+    const size_t words = (size_t)w.pairs * w.tiles * 2 * 16 * 4;
+    const size_t t = align_up(2 * sizeof(uint32_t));
+    const size_t v = align_up(words * sizeof(uint32_t));
+    const size_t pb = align_up((size_t)w.pairs * w.tiles * G * nq::kPartStride * sizeof(float));
+    char *b = (char *)base;
+    w.ticket = (uint32_t *)b;
+    w.agg = (uint32_t *)(b + t);
+    w.incl = (uint32_t *)(b + t + v);   // directly follows agg: one reset covers both
+    w.part = (float *)(b + t + 2 * v);
+    w.bytes = t + 2 * v + pb;
     return w;
 }
 
@@ -314,6 +341,90 @@ nq_status nq_decode(const nq_params *p, const int8_t *codes_k, const int8_t *cod
                        w.agg, words, w.ticket);
     hipLaunchKernelGGL(nq::k_decode, dim3((uint32_t)w.tiles), dim3(nq::kCodecThreads), 0, s, a);
     return launched("nq_decode");
+}
+
+size_t nq_decode_attend_workspace_bytes(const nq_params *p, int32_t q_heads)
+{
+    if (check(p) != NQ_OK || q_heads < 1 || q_heads % p->kv_heads) return 0;
+    return fused_ws(p, q_heads, nullptr).bytes;
+}
+
+nq_status nq_decode_attend(const nq_params *p, const int8_t *codes_k, const int8_t *codes_v,
+                           const void *scales_k, const void *scales_v, const int32_t *positions,
+                           const float *rope_cos, const float *rope_sin, const void *Q,
+                           int32_t q_heads, float *out, void *workspace, size_t ws_bytes,
+                           void *stream)
+{
+    nq_status st = check(p);
+    if (st != NQ_OK) return st;
+    if (q_heads < 1 || q_heads % p->kv_heads) return NQ_ERR_INVALID_ARG;
+    const int G = q_heads / p->kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return NQ_ERR_UNSUPPORTED;
+    const int32_t Lc = compressed_layers(p);
+    if (Lc == 0) return NQ_OK;
+    if (!Q || !out || !aligned(Q, 16) || !aligned(out, 16)) return NQ_ERR_INVALID_ARG;
+    const int32_t n = keep_count(p);
+    hipStream_t s = as_stream(stream);
+    if (n == 0) {   // nothing to attend to: zeros, written by a kernel (no memset node)
+        const int64_t words = (int64_t)Lc * q_heads * 128;
+        clear_error();
+        hipLaunchKernelGGL(nq::k_decode_reset, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0,
+                           s, (uint32_t *)out, words, (uint32_t *)out);
+        return launched("nq_decode_attend");
+    }
+    const void *ptrs16[] = {codes_k, codes_v, rope_cos, rope_sin};
+    for (const void *q : ptrs16)
+        if (!q || !aligned(q, 16)) return NQ_ERR_INVALID_ARG;
+    if (!positions || !aligned(positions, 4) || !scales_k || !scales_v || !aligned(scales_k, 16) ||
+        !aligned(scales_v, 16))
+        return NQ_ERR_INVALID_ARG;
+    const size_t need = fused_ws(p, q_heads, nullptr).bytes;
+    if (!workspace || ws_bytes < need || !aligned(workspace, kAlign)) return NQ_ERR_WORKSPACE;
+    FusedWs w = fused_ws(p, q_heads, workspace);
+    nq::FusedArgs a;
+    a.codes_k = codes_k;
+    a.codes_v = codes_v;
+    a.scales_k = (const uint16_t *)scales_k;
+    a.scales_v = (const uint16_t *)scales_v;
+    a.positions = positions;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
+    a.Q = (const uint16_t *)Q;
+    a.out = out;
+    a.part = w.part;
+    a.lb_agg = w.agg;
+    a.lb_incl = w.incl;
+    a.lb_ticket = w.ticket;
+    a.H = p->kv_heads;
+    a.Hq = q_heads;
+    a.T = p->tokens;
+    a.n_keep = n;
+    a.tiles = w.tiles;
+    clear_error();
+    const int64_t words = (int64_t)(w.incl - w.agg) + (int64_t)w.pairs * w.tiles * 2 * 64;
+    hipLaunchKernelGGL(nq::k_decode_reset, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0, s,
+                       w.agg, words, w.ticket);
+    const dim3 grid((uint32_t)((int64_t)w.pairs * w.tiles)), blk(nq::kCodecThreads);
+    const dim3 mgrid((uint32_t)(Lc * q_heads));
+    switch (G) {
+    case 1:
+        hipLaunchKernelGGL(nq::k_decode_attend<1>, grid, blk, 0, s, a);
+        hipLaunchKernelGGL(nq::k_decode_attend_merge<1>, mgrid, blk, 0, s, a);
+        break;
+    case 2:
+        hipLaunchKernelGGL(nq::k_decode_attend<2>, grid, blk, 0, s, a);
+        hipLaunchKernelGGL(nq::k_decode_attend_merge<2>, mgrid, blk, 0, s, a);
+        break;
+    case 4:
+        hipLaunchKernelGGL(nq::k_decode_attend<4>, grid, blk, 0, s, a);
+        hipLaunchKernelGGL(nq::k_decode_attend_merge<4>, mgrid, blk, 0, s, a);
+        break;
+    default:
+        hipLaunchKernelGGL(nq::k_decode_attend<8>, grid, blk, 0, s, a);
+        hipLaunchKernelGGL(nq::k_decode_attend_merge<8>, mgrid, blk, 0, s, a);
+        break;
+    }
+    return launched("nq_decode_attend");
 }
 
 nq_status nq_attend_decode(const nq_params *p, const void *Q, int32_t q_heads, const void *K,

@@ -392,13 +392,53 @@ __device__ __forceinline__ bool lb_read(const uint32_t *base, uint32_t tag, uint
            (w[3] >> 16) == tag;
 }
 
-// Reconstructs one token of one chain for this lane's 8 dims and stores it. code: the token's
-// absolute code bytes as c + 64, s16: this group's scale, (cr, sr): the rotary table row of the
-// token's position (keys only).
+// Decoupled look-back of one tile of a chain, run by the 16 lanes of one lane group (lane g
+// carries group g's 8 running bytes); they move together: a value is taken only when every
+// lane's words are complete. slot: this tile's word slot; the chain's previous tile sits
+// `step` slots earlier. Publishes this tile's aggregate (tile > 0) and inclusive prefix, and
+// returns the exclusive prefix. A wait longer than kSpinLimit sets *err and gives up.
+__device__ __forceinline__ uint2 chain_lookback(uint32_t *lb_agg, uint32_t *lb_incl, size_t slot,
+                                                size_t step, int tile, uint2 agg, int g,
+                                                uint32_t *err)
+{
+    uint2 excl = make_uint2(0u, 0u);
+    const size_t me = (slot * 16 + g) * 4;
+    if (tile == 0) {
+        lb_publish(lb_incl + me, agg, 2u);
+        return excl;
+    }
+    lb_publish(lb_agg + me, agg, 1u);
+    size_t pred = slot - step;
+    uint32_t spins = 0;
+    while (true) {
+        const size_t pw = (pred * 16 + g) * 4;
+        uint2 v;
+        if (__ballot(!lb_read(lb_incl + pw, 2u, v)) == 0ull) {
+            excl = make_uint2(add_bytes(excl.x, v.x), add_bytes(excl.y, v.y));
+            break;
+        }
+        if (__ballot(!lb_read(lb_agg + pw, 1u, v)) == 0ull) {
+            excl = make_uint2(add_bytes(excl.x, v.x), add_bytes(excl.y, v.y));
+            pred -= step;
+            spins = 0;
+            continue;
+        }
+        if (++spins > kSpinLimit) {   // never expected: report and give up the wait
+            if (g == 0) atomicOr(err, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    lb_publish(lb_incl + me, make_uint2(add_bytes(excl.x, agg.x), add_bytes(excl.y, agg.y)), 2u);
+    return excl;
+}
+
+// Reconstructs one token of one chain for this lane's 8 dims: x = group_sign(g) times the
+// reconstructed row (dims 8g..8g+7). code: the token's absolute code bytes as c + 64, s16:
+// this group's scale, (cr, sr): the rotary table row of the token's position (keys only).
 template <bool IS_KEY>
-__device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off, int j, int g,
-                                             uint2 code, uint32_t s16, const float cr[8],
-                                             const float sr[8])
+__device__ __forceinline__ void decode_row(int g, uint2 code, uint32_t s16, const float cr[8],
+                                           const float sr[8], float x[8])
 {
     // The in-lane butterflies (h = 1, 2, 4) run on the integer codes in packed fp16, where
     // they are exact (|sums| <= 8 * 16): each code byte c + 64 becomes the fp16 1024 + (c + 64)
@@ -436,7 +476,6 @@ __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off,
         : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3)
         : "v"(r0), "v"(r1), "v"(r2), "v"(r3));
     // fp16 half times fp32 scale in one v_fma_mix_f32 (product rounded once, + 0)
-    float x[8];
     asm("v_fma_mix_f32 %0, %8, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
         "v_fma_mix_f32 %4, %8, %12, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
         "v_fma_mix_f32 %2, %9, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
@@ -457,6 +496,16 @@ __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off,
         for (int k = 0; k < 8; k++)
             x[k] = __builtin_fmaf(sg, lane_xor8(x[k]) * sr[k], x[k] * cr[k]);
     }
+}
+
+// decode_row, then the row stored (fp32 or fp16) at row j of the chain starting at row_off
+template <bool IS_KEY>
+__device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off, int j, int g,
+                                             uint2 code, uint32_t s16, const float cr[8],
+                                             const float sr[8])
+{
+    float x[8];
+    decode_row<IS_KEY>(g, code, s16, cr, sr, x);
     const uint32_t sbit = (__popc(g & 15) & 1) ? 0x80000000u : 0u;   // group_sign as a sign bit
     const size_t o = row_off + (size_t)j * kHeadDim + 8 * g;
     if (a.out_f32) {
@@ -491,54 +540,49 @@ struct DecodeShared {
     uint4 delta[kDecTile * kHeadDim / 16];        // the tile's delta codes
 };
 
-template <bool IS_KEY>
-__device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int ticket, int chains,
-                            DecodeShared &sh)
+// Loads a tile of one chain into LDS: nt (<= kDecTile) rows of delta codes and scales starting
+// at chain row `row0`, and, when pos is not null, the nt positions (clamped into [0, T)). Every
+// load of a thread is issued before its first LDS store, so they are in flight together (one
+// memory latency per tile, not one per chunk). The caller synchronises before reading.
+__device__ __forceinline__ void stage_tile(const int8_t *codes, const uint16_t *scales,
+                                           size_t row0, int nt, const int32_t *pos, int T,
+                                           uint4 *s_delta, uint4 *s_scale, int32_t *s_pos)
 {
-    auto &s_tot = sh.tot;
-    auto &s_excl = sh.excl;
-    auto &s_pos = sh.pos;
-    auto &s_scale = sh.scale;
+    constexpr int kDeltaChunks = kDecTile * kHeadDim / 16 / kCodecThreads;
+    static_assert(kDecTile * kGroups * 2 / 16 <= kCodecThreads && kDecTile <= kCodecThreads,
+                  "one scale chunk and one position per thread");
+    const u32x4 *dc = reinterpret_cast<const u32x4 *>(codes + row0 * kHeadDim);
+    const u32x4 *sc = reinterpret_cast<const u32x4 *>(scales + row0 * kGroups);
+    const int tid = threadIdx.x;
+    u32x4 d[kDeltaChunks], sv = {0u, 0u, 0u, 0u};
+    int pv = 0;
+#pragma unroll
+    for (int k = 0; k < kDeltaChunks; k++)
+        if (tid + k * kCodecThreads < 8 * nt)
+            d[k] = __builtin_nontemporal_load(dc + tid + k * kCodecThreads);
+    if (tid < 2 * nt) sv = __builtin_nontemporal_load(sc + tid);
+    if (pos && tid < nt) pv = pos[tid];
+#pragma unroll
+    for (int k = 0; k < kDeltaChunks; k++)
+        if (tid + k * kCodecThreads < 8 * nt)
+            s_delta[tid + k * kCodecThreads] = make_uint4(d[k].x, d[k].y, d[k].z, d[k].w);
+    if (tid < 2 * nt) s_scale[tid] = make_uint4(sv.x, sv.y, sv.z, sv.w);
+    if (pos && tid < nt) s_pos[tid] = min(max(pv, 0), T - 1);
+}
+
+// The running code of this lane's group just before lane group q's first token of a staged
+// tile (q walks tile rows q * kDecRun ..), as c + 64 per byte (|c| <= 16 keeps every byte in
+// range, so later steps add whole dwords without carries between bytes). Synchronises the
+// block before reading the tile and after the look-back; slot/step/err as in chain_lookback.
+__device__ __forceinline__ uint2 tile_run_base(const uint4 *s_delta, int nt, int q, int g,
+                                               uint2 (*s_tot)[16], uint2 *s_excl,
+                                               uint32_t *lb_agg, uint32_t *lb_incl, size_t slot,
+                                               size_t step, int tile, uint32_t *err)
+{
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane_group(lane & 15), q = wave * 4 + (lane >> 4);
-    const int n_keep = a.n_keep;
-    const size_t chain = (size_t)lc * a.H + h;
-    const int t0 = tile * kDecTile;
-    const int nt = min(kDecTile, n_keep - t0);
-    const int j0 = t0 + q * kDecRun;
-
-    // 0. stage the tile's positions and scales in LDS with coalesced loads; they arrive while the
-    //    running sum and the look-back below proceed
-    {
-        // every load of a thread is issued before the first LDS store, so they are in flight
-        // together (one memory latency per tile, not one per chunk)
-        constexpr int kDeltaChunks = kDecTile * kHeadDim / 16 / kCodecThreads;
-        static_assert(kDecTile * kGroups * 2 / 16 <= kCodecThreads && kDecTile <= kCodecThreads,
-                      "one scale chunk and one position per thread");
-        const u32x4 *dc = reinterpret_cast<const u32x4 *>(
-            (IS_KEY ? a.codes_k : a.codes_v) + (chain * (size_t)n_keep + t0) * kHeadDim);
-        const u32x4 *sc = reinterpret_cast<const u32x4 *>(
-            (IS_KEY ? a.scales_k : a.scales_v) + (chain * (size_t)n_keep + t0) * kGroups);
-        const int tid = threadIdx.x;
-        u32x4 d[kDeltaChunks], sv = {0u, 0u, 0u, 0u};
-        int pv = 0;
-#pragma unroll
-        for (int k = 0; k < kDeltaChunks; k++)
-            if (tid + k * kCodecThreads < 8 * nt)
-                d[k] = __builtin_nontemporal_load(dc + tid + k * kCodecThreads);
-        if (tid < 2 * nt) sv = __builtin_nontemporal_load(sc + tid);
-        if (IS_KEY && tid < nt) pv = a.positions[(size_t)lc * n_keep + t0 + tid];
-#pragma unroll
-        for (int k = 0; k < kDeltaChunks; k++)
-            if (tid + k * kCodecThreads < 8 * nt)
-                sh.delta[tid + k * kCodecThreads] = make_uint4(d[k].x, d[k].y, d[k].z, d[k].w);
-        if (tid < 2 * nt) s_scale[tid] = make_uint4(sv.x, sv.y, sv.z, sv.w);
-        if (IS_KEY && tid < nt) s_pos[tid] = min(max(pv, 0), a.T - 1);
-    }
-
-    // 1. the byte-wise sum of this lane group's deltas (from the staged tile)
+    // 1. the byte-wise sum of this lane group's deltas
     __syncthreads();
-    const uint2 *sd = reinterpret_cast<const uint2 *>(sh.delta) + g;   // [token][16 lanes]
+    const uint2 *sd = reinterpret_cast<const uint2 *>(s_delta) + g;   // [token][16 lanes]
     uint2 acc = make_uint2(0u, 0u);
 #pragma unroll
     for (int i = 0; i < kDecRun; i++) {
@@ -566,52 +610,49 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
         incl = make_uint2(add_bytes(incl.x, t.x), add_bytes(incl.y, t.y));
     }
     const uint2 gp = make_uint2(sub_bytes(incl.x, acc.x), sub_bytes(incl.y, acc.y));
-    // 3. decoupled look-back, done by lane group 15 (it holds the tile total); the 16 lanes of
-    //    the group move together: a value is taken only when every lane's words are complete
-    if (q == 15) {
-        const uint2 agg = make_uint2(add_bytes(gp.x, acc.x), add_bytes(gp.y, acc.y));
-        uint2 excl = make_uint2(0u, 0u);
-        const size_t me = ((size_t)ticket * 16 + g) * 4;
-        if (tile == 0) {
-            lb_publish(a.lb_incl + me, agg, 2u);
-        } else {
-            lb_publish(a.lb_agg + me, agg, 1u);
-            int pred = ticket - chains;          // the previous tile of this chain
-            uint32_t spins = 0;
-            while (true) {
-                const size_t pw = ((size_t)pred * 16 + g) * 4;
-                uint2 v;
-                if (__ballot(!lb_read(a.lb_incl + pw, 2u, v)) == 0ull) {
-                    excl = make_uint2(add_bytes(excl.x, v.x), add_bytes(excl.y, v.y));
-                    break;
-                }
-                if (__ballot(!lb_read(a.lb_agg + pw, 1u, v)) == 0ull) {
-                    excl = make_uint2(add_bytes(excl.x, v.x), add_bytes(excl.y, v.y));
-                    pred -= chains;
-                    spins = 0;
-                    continue;
-                }
-                if (++spins > kSpinLimit) {   // never expected: report and give up the wait
-                    if (g == 0) atomicOr(&a.lb_ticket[1], 1u);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            lb_publish(a.lb_incl + me,
-                       make_uint2(add_bytes(excl.x, agg.x), add_bytes(excl.y, agg.y)), 2u);
-        }
-        s_excl[g] = excl;
-    }
+    // 3. decoupled look-back, done by lane group 15 (it holds the tile total)
+    if (q == 15)
+        s_excl[g] = chain_lookback(lb_agg, lb_incl, slot, step, tile,
+                                   make_uint2(add_bytes(gp.x, acc.x), add_bytes(gp.y, acc.y)), g,
+                                   err);
     __syncthreads();
     const uint2 base0 = s_excl[g];
-    // the running code before this group's first token, as c + 64 (|c| <= 16 keeps every byte
-    // in range, so later steps add whole dwords without carries between bytes)
-    uint2 run = make_uint2(add_bytes(base0.x, gp.x), add_bytes(base0.y, gp.y));
-    run = make_uint2((run.x ^ 0x80808080u) - 0x40404040u, (run.y ^ 0x80808080u) - 0x40404040u);
+    const uint2 run = make_uint2(add_bytes(base0.x, gp.x), add_bytes(base0.y, gp.y));
+    return make_uint2((run.x ^ 0x80808080u) - 0x40404040u, (run.y ^ 0x80808080u) - 0x40404040u);
+}
+
+// (c + 64) + (d + 128) - 128 per byte, d two's complement with |d| <= 32: every byte stays
+// within [16, 240], so one 32-bit add3 is the byte-wise sum
+__device__ __forceinline__ uint2 run_step(uint2 run, uint2 d)
+{
+    return make_uint2(run.x + (d.x ^ 0x80808080u) + 0x7f7f7f80u,
+                      run.y + (d.y ^ 0x80808080u) + 0x7f7f7f80u);
+}
+
+template <bool IS_KEY>
+__device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int ticket, int chains,
+                            DecodeShared &sh)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane_group(lane & 15), q = wave * 4 + (lane >> 4);
+    const int n_keep = a.n_keep;
+    const size_t chain = (size_t)lc * a.H + h;
+    const int t0 = tile * kDecTile;
+    const int nt = min(kDecTile, n_keep - t0);
+    const int j0 = t0 + q * kDecRun;
+    const int32_t *s_pos = sh.pos;
+
+    stage_tile(IS_KEY ? a.codes_k : a.codes_v, IS_KEY ? a.scales_k : a.scales_v,
+               chain * (size_t)n_keep + t0, nt,
+               IS_KEY ? a.positions + (size_t)lc * n_keep + t0 : nullptr, a.T, sh.delta,
+               sh.scale, sh.pos);
+    uint2 run = tile_run_base(sh.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
+                              (size_t)ticket, (size_t)chains, tile, a.lb_ticket + 1);
+    const uint2 *sd = reinterpret_cast<const uint2 *>(sh.delta) + g;   // [token][16 lanes]
     // 4. reconstruct every token of this lane group; the next token's rotary rows are requested
     //    before the current token is computed
     const size_t row_off = chain * (size_t)n_keep * kHeadDim;
-    const uint16_t *sl = reinterpret_cast<const uint16_t *>(s_scale);
+    const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.scale);
     const int jend = min(n_keep, j0 + kDecRun);
     float cn[8], sn[8];
     if (IS_KEY && j0 < jend) {
@@ -633,11 +674,7 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
                     load_f32x8(a.rope_sin + p, sn);
                 }
             }
-            // (c + 64) + (d + 128) - 128 per byte, d two's complement with |d| <= 32: every
-            // byte stays within [16, 240], so one 32-bit add3 is the byte-wise sum
-            const uint2 d = sd[(j - t0) * 16];
-            run = make_uint2(run.x + (d.x ^ 0x80808080u) + 0x7f7f7f80u,
-                             run.y + (d.y ^ 0x80808080u) + 0x7f7f7f80u);
+            run = run_step(run, sd[(j - t0) * 16]);
             decode_store<IS_KEY>(a, row_off, j, g, run, sl[(j - t0) * kGroups + g], cr, sr);
         }
     }

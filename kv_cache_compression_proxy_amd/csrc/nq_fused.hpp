@@ -1,0 +1,290 @@
+// One-token grouped-query attention straight from the compressed cache: the delta codes and
+// scales are decoded inside the attention kernel and the reconstructed K/V never reach HBM
+// (the VQKV page, "推理流程集成": reconstruct on demand while decoding, attending over the
+// reconstructed cache).
+//
+// A block owns one tile of kDecTile kept tokens of one (layer, kv head) pair and the G query
+// heads that share that kv head. Keys: the K chain's running codes come from the same staged
+// scan and decoupled look-back as nq_decode; each key row is rebuilt in registers (inverse
+// Hadamard, RoPE at its position) and dotted with the G queries. Values: because
+// v_t = H x_t / sqrt(128) with x_t = s_t c_t / 2 and H linear, the softmax-weighted sum of the
+// values is H (sum_t p_t x_t) / sqrt(128) -- the tile accumulates sum_t p_t x_t on the codes
+// directly and the inverse Hadamard runs once per query head in the merge kernel. Tiles write
+// (max, sum, accumulator) partials; the merge combines them (flash-decoding style).
+#pragma once
+
+#include "nq_codec.hpp"
+
+namespace nq {
+
+struct FusedArgs {
+    const int8_t *codes_k, *codes_v;      // [Lc][H][n][128], delta-coded
+    const uint16_t *scales_k, *scales_v;  // [Lc][H][n][16] fp16
+    const int32_t *positions;             // [Lc][n]
+    const float *rope_cos, *rope_sin;     // [T][64]
+    const uint16_t *Q;                    // [Lc][Hq][128] fp16
+    float *out;                           // [Lc][Hq][128]
+    float *part;                          // [pairs][tiles][G][kPartStride]
+    uint32_t *lb_agg, *lb_incl, *lb_ticket;
+    int32_t H, Hq, T, n_keep, tiles;      // tiles per pair
+};
+
+// a tile partial per query head: running max, sum of weights, then 128 accumulated dims
+constexpr int kPartStride = 2 + kHeadDim;
+
+template <int G>
+struct FusedShared {
+    uint2 tot[4][16];
+    uint2 excl[16];
+    int32_t pos[kDecTile];
+    float z[kDecTile][G];   // scores, then weights exp(z - m)
+    float ml[G][2];         // the tile's max and sum per query head
+    union {
+        struct {
+            uint4 scale[kDecTile * kGroups * 2 / 16];
+            uint4 delta[kDecTile * kHeadDim / 16];
+        } t;
+        float red[4][G][16][9];   // per-wave sums of the value accumulators
+    } u;
+};
+
+// sum over the 16 lanes of a row (every lane gets the sum); xor partners 1, 2, 7, 8 generate
+// all 16 lanes
+__device__ __forceinline__ float row_sum16(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kDppRor8, 0xF, 0xF, true));
+    return v;
+}
+
+// grid: pairs * tiles blocks (pairs = Lc * H); tickets tile-major over the pairs as in
+// k_decode. Look-back slots: 2 * ticket + tensor (K = 0, V = 1).
+template <int G>
+__global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
+{
+    __shared__ int s_ticket;
+    __shared__ FusedShared<G> sh;
+    if (threadIdx.x == 0) s_ticket = (int)atomicAdd(&a.lb_ticket[0], 1u);
+    __syncthreads();
+    const int ticket = s_ticket;
+    const int pairs = (int)(gridDim.x / (uint32_t)a.tiles);
+    const int tile = ticket / pairs;
+    const int pair = ticket % pairs;
+    const int h = pair % a.H, lc = pair / a.H;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane_group(lane & 15), q = wave * 4 + (lane >> 4);
+    const int n_keep = a.n_keep;
+    const int t0 = tile * kDecTile;
+    const int nt = min(kDecTile, n_keep - t0);
+    const int jl0 = q * kDecRun;                       // this lane group's first tile row
+    const size_t row0 = (size_t)pair * n_keep + t0;    // chain row of the tile's first token
+
+    // queries of this kv head, this lane's 8 dims, times group_sign(g) / sqrt(128): the keys
+    // come out of decode_row with group_sign(g) applied, so q . x is the true score
+    float qv[G][8];
+    {
+        const float f = group_sign(g) * kInvSqrt128;
+#pragma unroll
+        for (int i = 0; i < G; i++) {
+            load_f16x8(a.Q + ((size_t)lc * a.Hq + h * G + i) * kHeadDim + 8 * g, qv[i]);
+#pragma unroll
+            for (int k = 0; k < 8; k++) qv[i][k] *= f;
+        }
+    }
+
+    // ---- keys: scores z[t][i] of the tile
+    stage_tile(a.codes_k, a.scales_k, row0, nt, a.positions + (size_t)lc * n_keep + t0, a.T,
+               sh.u.t.delta, sh.u.t.scale, sh.pos);
+    {
+        uint2 run = tile_run_base(sh.u.t.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
+                                  2 * (size_t)ticket, 2 * (size_t)pairs, tile, a.lb_ticket + 1);
+        const uint2 *sd = reinterpret_cast<const uint2 *>(sh.u.t.delta) + g;
+        const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.u.t.scale);
+        const int jend = min(nt, jl0 + kDecRun);
+        float cn[8], sn[8];
+        if (jl0 < jend) {
+            const size_t p = (size_t)sh.pos[jl0] * 64 + 8 * (g & 7);
+            load_f32x8(a.rope_cos + p, cn);
+            load_f32x8(a.rope_sin + p, sn);
+        }
+#pragma unroll
+        for (int i = 0; i < kDecRun; i++) {
+            const int jl = jl0 + i;
+            if (jl < jend) {
+                float cr[8], sr[8];
+#pragma unroll
+                for (int k = 0; k < 8; k++) { cr[k] = cn[k]; sr[k] = sn[k]; }
+                if (jl + 1 < jend) {
+                    const size_t p = (size_t)sh.pos[jl + 1] * 64 + 8 * (g & 7);
+                    load_f32x8(a.rope_cos + p, cn);
+                    load_f32x8(a.rope_sin + p, sn);
+                }
+                run = run_step(run, sd[jl * 16]);
+                float x[8];
+                decode_row<true>(g, run, sl[jl * kGroups + g], cr, sr, x);
+#pragma unroll
+                for (int hq = 0; hq < G; hq++) {
+                    float d = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < 8; k++) d = __builtin_fmaf(qv[hq][k], x[k], d);
+                    d = row_sum16(d);
+                    if ((lane & 15) == 0) sh.z[jl][hq] = d;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- softmax within the tile: wave w handles query heads w, w + 4, ...; 2 rows per lane
+    for (int hq = wave; hq < G; hq += 4) {
+        const float z0 = lane < nt ? sh.z[lane][hq] : -INFINITY;
+        const float z1 = lane + 64 < nt ? sh.z[lane + 64][hq] : -INFINITY;
+        float m = fmaxf(z0, z1);
+#pragma unroll
+        for (int msk = 1; msk < 64; msk <<= 1) m = fmaxf(m, __shfl_xor(m, msk));
+        const float p0 = lane < nt ? expf(z0 - m) : 0.0f;
+        const float p1 = lane + 64 < nt ? expf(z1 - m) : 0.0f;
+        float l = p0 + p1;
+#pragma unroll
+        for (int msk = 1; msk < 64; msk <<= 1) l += __shfl_xor(l, msk);
+        if (lane < nt) sh.z[lane][hq] = p0;
+        if (lane + 64 < nt) sh.z[lane + 64][hq] = p1;
+        if (lane == 0) { sh.ml[hq][0] = m; sh.ml[hq][1] = l; }
+    }
+    __syncthreads();   // also: every key row has been read, the staging area may be reused
+
+    // ---- values: acc[i][k] = sum_t p_t,i * (s_t / 2) * (c_t,k + 64), W[i] = sum_t p_t,i s_t / 2
+    stage_tile(a.codes_v, a.scales_v, row0, nt, nullptr, a.T, sh.u.t.delta, sh.u.t.scale,
+               nullptr);
+    float acc[G][8], W[G];
+#pragma unroll
+    for (int i = 0; i < G; i++) {
+        W[i] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; k++) acc[i][k] = 0.0f;
+    }
+    {
+        uint2 run = tile_run_base(sh.u.t.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
+                                  2 * (size_t)ticket + 1, 2 * (size_t)pairs, tile,
+                                  a.lb_ticket + 1);
+        const uint2 *sd = reinterpret_cast<const uint2 *>(sh.u.t.delta) + g;
+        const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.u.t.scale);
+        const int jend = min(nt, jl0 + kDecRun);
+#pragma unroll
+        for (int i = 0; i < kDecRun; i++) {
+            const int jl = jl0 + i;
+            if (jl < jend) {
+                run = run_step(run, sd[jl * 16]);
+                const float hs = 0.5f * h2f(sl[jl * kGroups + g]);
+                float b[8];
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    b[k] = (float)((run.x >> (8 * k)) & 0xffu);
+                    b[k + 4] = (float)((run.y >> (8 * k)) & 0xffu);
+                }
+#pragma unroll
+                for (int hq = 0; hq < G; hq++) {
+                    const float w = sh.z[jl][hq] * hs;
+                    W[hq] += w;
+#pragma unroll
+                    for (int k = 0; k < 8; k++) acc[hq][k] = __builtin_fmaf(w, b[k], acc[hq][k]);
+                }
+            }
+        }
+    }
+    // remove the +64 offset: acc = sum w (c + 64) - 64 sum w
+#pragma unroll
+    for (int hq = 0; hq < G; hq++)
+#pragma unroll
+        for (int k = 0; k < 8; k++) acc[hq][k] = __builtin_fmaf(-64.0f, W[hq], acc[hq][k]);
+    // sum over the 4 rows of the wave (lane distance 16, 32), then over the 4 waves in LDS
+#pragma unroll
+    for (int msk = 16; msk < 64; msk <<= 1)
+#pragma unroll
+        for (int hq = 0; hq < G; hq++)
+#pragma unroll
+            for (int k = 0; k < 8; k++) acc[hq][k] += __shfl_xor(acc[hq][k], msk);
+    __syncthreads();   // the value rows are no longer read: the staging area becomes red
+    if (lane < 16) {
+#pragma unroll
+        for (int hq = 0; hq < G; hq++)
+#pragma unroll
+            for (int k = 0; k < 8; k++) sh.u.red[wave][hq][lane][k] = acc[hq][k];
+    }
+    __syncthreads();
+    // partial of query head hq: [m, l, acc in natural dim order]
+    float *part = a.part + ((size_t)pair * a.tiles + tile) * G * kPartStride;
+    for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kCodecThreads) {
+        const int hq = idx / kHeadDim, r = idx % kHeadDim;   // r = lane slot * 8 + k
+        const int l16 = r >> 3, k = r & 7;
+        const float v = sh.u.red[0][hq][l16][k] + sh.u.red[1][hq][l16][k] +
+                        sh.u.red[2][hq][l16][k] + sh.u.red[3][hq][l16][k];
+        part[hq * kPartStride + 2 + 8 * lane_group(l16) + k] = v;
+    }
+    if (threadIdx.x < G) {
+        part[threadIdx.x * kPartStride] = sh.ml[threadIdx.x][0];
+        part[threadIdx.x * kPartStride + 1] = sh.ml[threadIdx.x][1];
+    }
+}
+
+// One block of 256 threads per (layer, query head): the 16 lane groups combine the tiles of the
+// pair (online max / sum), merge through LDS, then lane group 0 applies the inverse Hadamard to
+// the weighted code sum and divides by the weight sum: o = H acc / (sqrt(128) l).
+template <int G>
+__global__ __launch_bounds__(kCodecThreads) void k_decode_attend_merge(FusedArgs a)
+{
+    __shared__ float s_m[16], s_l[16];
+    __shared__ float s_acc[16][kHeadDim];
+    const int lj = blockIdx.x;
+    const int lc = lj / a.Hq, j = lj % a.Hq;
+    const int h = j / G, hq = j % G;
+    const int pair = lc * a.H + h;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane_group(lane & 15), q = wave * 4 + (lane >> 4);
+    float m = -INFINITY, l = 0.0f, acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) acc[k] = 0.0f;
+    for (int t = q; t < a.tiles; t += 16) {
+        const float *pp = a.part + (((size_t)pair * a.tiles + t) * G + hq) * kPartStride;
+        const float m2 = pp[0], l2 = pp[1];
+        float a2[8];
+#pragma unroll
+        for (int k = 0; k < 8; k++) a2[k] = pp[2 + 8 * g + k];
+        const float M = fmaxf(m, m2);
+        if (M != -INFINITY) {
+            const float f1 = expf(m - M), f2 = expf(m2 - M);
+            l = l * f1 + l2 * f2;
+#pragma unroll
+            for (int k = 0; k < 8; k++) acc[k] = acc[k] * f1 + a2[k] * f2;
+            m = M;
+        }
+    }
+    if ((lane & 15) == 0) { s_m[q] = m; s_l[q] = l; }
+#pragma unroll
+    for (int k = 0; k < 8; k++) s_acc[q][8 * g + k] = acc[k];
+    __syncthreads();
+    if (q != 0) return;
+    float M = -INFINITY;
+    for (int r = 0; r < 16; r++) M = fmaxf(M, s_m[r]);
+    float L = 0.0f, x[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) x[k] = 0.0f;
+    if (M != -INFINITY) {
+        for (int r = 0; r < 16; r++) {
+            const float f = expf(s_m[r] - M);
+            L += s_l[r] * f;
+#pragma unroll
+            for (int k = 0; k < 8; k++) x[k] = __builtin_fmaf(s_acc[r][8 * g + k], f, x[k]);
+        }
+    }
+    hadamard_butterflies(x, g);   // x = group_sign(g) * H acc
+    const float f = L > 0.0f ? group_sign(g) * kInvSqrt128 / L : 0.0f;
+    float *o = a.out + ((size_t)lc * a.Hq + j) * kHeadDim + 8 * g;
+#pragma unroll
+    for (int k = 0; k < 8; k++) o[k] = x[k] * f;
+}
+
+}  // namespace nq

@@ -107,6 +107,19 @@ def test_pointer_and_workspace_errors_before_launch():
     with pytest.raises(nq.NqError) as ei:                       # G = 16 unsupported
         nq.nq_attend_decode(p, fake, 128, fake, fake, 10, fake, None, stream=0)
     assert ei.value.status == nq.NQ_ERR_UNSUPPORTED
+    # fused decode + attention
+    assert nq.nq_decode_attend_workspace_bytes(p, 12) == 0                # 12 % 8 != 0
+    fn = nq.nq_decode_attend_workspace_bytes(p, 32)
+    assert fn > nq.nq_decode_attend_workspace_bytes(p, 8) > 0            # partials grow with G
+    h = lib.nq_decode_attend
+    h.argtypes = [C.POINTER(nq.NqParams)] + [C.c_void_p] * 8 + [C.c_int32, C.c_void_p,
+                                                                 C.c_void_p, C.c_size_t,
+                                                                 C.c_void_p]
+    assert h(C.byref(p), *([fake] * 8), 24, fake, fake, fn, None) == nq.NQ_ERR_UNSUPPORTED  # G=3
+    assert h(C.byref(p), *([fake] * 8), 20, fake, fake, fn, None) == nq.NQ_ERR_INVALID_ARG
+    assert h(C.byref(p), *([fake] * 8), 32, fake + 4, fake, fn, None) == nq.NQ_ERR_INVALID_ARG
+    assert h(C.byref(p), *([fake] * 8), 32, fake, fake, fn - 1, None) == nq.NQ_ERR_WORKSPACE
+    assert h(C.byref(p), *([fake] * 8), 32, fake, fake + 16, fn, None) == nq.NQ_ERR_WORKSPACE
 
 
 def test_status_strings():

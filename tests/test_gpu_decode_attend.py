@@ -1,0 +1,108 @@
+"""GPU parity of the fused decode + GQA attention (nq_decode_attend) against the oracle.
+
+The GPU is fed the oracle's own compressed layers (codes, scales, positions from
+oracle.compress_layer), so only the fused kernel is under test. The oracle's reference is its
+decode (oracle.decode_layer, fp64) followed by its attention (oracle.attend_layer, fp64) over
+those reconstructions, with no fp16 rounding in between -- the fused path never materialises
+K_hat/V_hat. Tolerance: max |gpu - oracle| / max |v_hat| per (layer, query head) <= 1e-5 (fp32
+scores, exponentials and sums against fp64; the attention check's own bar is 1e-3).
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_proxy_amd as nq
+import kvsynth
+import oracle
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+FUSED_TOL = 1e-5
+
+# (tokens, window, evict_permille, G, layers, protect_boundary): several 128-token tiles with a
+# ragged tail, a single partial tile, a tile holding one token, a one-token cache, and a
+# protected-boundary layer range (layer 1 of 3 compressed)
+CASES = [
+    (2048, 128, 600, 4, 2, 0),
+    (300, 64, 600, 1, 1, 0),
+    (129, 16, 0, 2, 1, 0),
+    (1, 4, 600, 8, 1, 0),
+    (1000, 32, 800, 8, 3, 1),
+]
+
+
+def oracle_layers(w, T, layers):
+    Ct, St = oracle.rope_table(T, w.rope_base)
+    encs = []
+    for l in layers:
+        K_l, V_l = kvsynth.layer_kv(w, l, T)
+        encs.append(oracle.compress_layer(K_l, V_l, w.window, w.evict_permille, w.bits_k,
+                                          w.bits_v, Ct, St))
+    return encs, Ct, St
+
+
+@pytest.mark.parametrize("T,W,e,G,L,pb", CASES)
+def test_decode_attend_on_oracle_cache(T, W, e, G, L, pb):
+    w = kvsynth.workload(0).with_(tokens=T, window=W, evict_permille=e, layers=L,
+                                  protect_boundary=pb)
+    lb, le = w.layer_begin, w.layer_end
+    H = w.kv_heads
+    encs, Ct, St = oracle_layers(w, T, range(lb, le))
+    p = nq.make_params(L, H, T, W, e, w.bits_k, w.bits_v, w.rope_base, lb, le)
+    n = nq.nq_keep_count(p)
+    assert all(enc["positions"].size == n for enc in encs)
+    say(f"[decode-attend] T={T} W={W} e={e} G={G} layers [{lb},{le}) of {L}: n_keep={n}")
+    dev = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(np.stack(a))).to(dev)
+    ck = t([enc["codes_k"] for enc in encs])
+    cv = t([enc["codes_v"] for enc in encs])
+    sk = t([enc["scales_k"].view(np.float16) for enc in encs])
+    sv = t([enc["scales_v"].view(np.float16) for enc in encs])
+    pos = t([enc["positions"] for enc in encs])
+    cos, sin = nq.rope_table(p, dev)
+    Lc = le - lb
+    q = np.random.default_rng(1000 * G + T).standard_normal((Lc, G * H, 128)).astype(np.float16)
+    out = torch.full((Lc, G * H, 128), float("nan"), dtype=torch.float32, device=dev)
+    ws = nq.workspace(nq.nq_decode_attend_workspace_bytes(p, G * H), dev)
+    nq.nq_decode_attend(p, ck, cv, sk, sv, pos, cos, sin, torch.from_numpy(q).to(dev), G * H,
+                        out, ws)
+    torch.cuda.synchronize()
+    assert int(ws[:8].cpu().numpy().view(np.uint32)[1]) == 0   # no look-back wait gave up
+    got = out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for lc, enc in enumerate(encs):
+        Kh, Vh = oracle.decode_layer(enc["codes_k"], enc["codes_v"], enc["scales_k"],
+                                     enc["scales_v"], enc["positions"], Ct, St)
+        ref = oracle.attend_layer(q[lc], Kh, Vh)
+        vmax = np.abs(Vh).max(axis=(1, 2)).repeat(G)   # per query head, its kv head's max
+        err = np.abs(got[lc] - ref).max(axis=1) / np.maximum(vmax, 1e-30)
+        worst = max(worst, float(err.max()))
+    say(f"[decode-attend] max err / max|v| = {worst:.3g}")
+    assert worst <= FUSED_TOL
+
+
+def test_decode_attend_repeatable():
+    """Two calls on one workspace give bitwise equal outputs (the look-back words and the
+    ticket are reset by every call)."""
+    T, W, e, G = 2048, 128, 600, 4
+    w = kvsynth.workload(0).with_(tokens=T, window=W, evict_permille=e)
+    encs, _, _ = oracle_layers(w, T, [0])
+    p = nq.make_params(1, w.kv_heads, T, W, e, w.bits_k, w.bits_v, w.rope_base)
+    dev = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a[None])).to(dev)
+    enc = encs[0]
+    args = (t(enc["codes_k"]), t(enc["codes_v"]), t(enc["scales_k"].view(np.float16)),
+            t(enc["scales_v"].view(np.float16)), t(enc["positions"]))
+    cos, sin = nq.rope_table(p, dev)
+    Hq = G * w.kv_heads
+    Q = torch.from_numpy(np.random.default_rng(7).standard_normal((1, Hq, 128))
+                         .astype(np.float16)).to(dev)
+    ws = nq.workspace(nq.nq_decode_attend_workspace_bytes(p, Hq), dev)
+    outs = []
+    for _ in range(2):
+        o = torch.empty((1, Hq, 128), dtype=torch.float32, device=dev)
+        nq.nq_decode_attend(p, *args, cos, sin, Q, Hq, o, ws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])

@@ -19,6 +19,7 @@ from test_gpu_parity import check_layer
 pytestmark = pytest.mark.gpu
 
 ATT_TOL = 1e-3   # max|gpu - oracle| / max|v_hat| per (layer, query head)
+FUSED_FULL_TOL = 1e-4   # the fused path at 26K tokens (fp32 sums against fp64)
 
 
 def sampled_layers(n):
@@ -62,12 +63,16 @@ def test_fullsize_workload(idx):
 
 def test_fullsize_longctx_and_decode_step():
     """The long-context max preset (workload 2) and the decode step over its output
-    (workload 4): 32 query heads over 8 kv heads, one fp16 query token per layer."""
+    (workload 4): 32 query heads over 8 kv heads, one fp16 query token per layer, by the
+    two-call path (fp16 reconstruction, then attention) and by the fused nq_decode_attend."""
     w, p, K, V, run = run_full(2)
     check_sampled(w, p, run)
     w4 = kvsynth.workload(4)
     Q = torch.from_numpy(kvsynth.queries(w4)).to("cuda")
     out = nq.attend(p, Q, run.K_hat, run.V_hat)
+    c = nq.Compressed(p, run.positions, run.codes_k, run.codes_v, run.scales_k, run.scales_v,
+                      run.cos, run.sin)
+    fused = nq.attend_compressed(c, Q)
     torch.cuda.synchronize()
     Ct, St = oracle.rope_table(w.tokens, w.rope_base)
     for lc in (0, w.compressed_layers - 1):
@@ -87,3 +92,10 @@ def test_fullsize_longctx_and_decode_step():
         err = np.abs(got - ref).max(axis=1) / vmax
         say(f"[decode-step] layer {lc}: max err / max|v| = {err.max():.3g}")
         assert err.max() <= ATT_TOL
+        # the fused path, from the same compressed cache, against the oracle's attention over
+        # its fp64 reconstruction (the fused path rounds nothing to fp16)
+        reff = oracle.attend_layer(Q[lc].cpu().numpy(), Kh, Vh)
+        gotf = fused[lc].cpu().numpy().astype(np.float64)
+        errf = np.abs(gotf - reff).max(axis=1) / np.abs(Vh).max(axis=(1, 2)).repeat(G)
+        say(f"[decode-step] fused, layer {lc}: max err / max|v| = {errf.max():.3g}")
+        assert errf.max() <= FUSED_FULL_TOL
