@@ -122,8 +122,9 @@ nq_status nq_encode(const nq_params *p, const void *K, const void *V, const int3
 
 /* Inverse of nq_encode ("技术实现细节": RoPE is restored after quantization): running sum of the
  * deltas mod 256 -> c; x = s * c / 2; inverse normalised Hadamard transform; keys rotated
- * forward by their stored position. Inputs as produced by nq_encode: the running codes must stay
- * within [-64, 63] (nq_encode's stay within [-16, 16]); other byte streams decode to unspecified
+ * forward by their stored position. Inputs as produced by nq_encode: every running code must
+ * stay within [-16, 16] (nq_encode's do: |c| <= 2 rho_b + 1 <= 15, 16 only on an exact
+ * parity tie), so every delta lies in [-32, 32]; other byte streams decode to unspecified
  * values.
  *   K_out, V_out  [L_c][H][n_keep][128] out, fp16 or fp32 per out_dtype
  *   workspace     device scratch of nq_decode_workspace_bytes(p) bytes (tile prefixes of the

@@ -392,16 +392,42 @@ __device__ __forceinline__ bool lb_read(const uint32_t *base, uint32_t tag, uint
            (w[3] >> 16) == tag;
 }
 
+// Running sums of the delta chain in offset-64 form: a byte holds v + 64. Every value the
+// scans handle is a difference of two running codes or a running code (|c| <= 16), so it lies
+// in [-32, 32] and every byte of every intermediate below stays inside [0, 255]: whole 32-bit
+// adds act byte-wise, with no carry or borrow between bytes.
+constexpr uint32_t kOff64 = 0x40404040u;   // zero in offset-64 form
+
+// v + d per byte, d a two's complement delta: (v + 64) + (d + 128) - 128 (the intermediate
+// (v + d) + 192 stays within [160, 224])
+__device__ __forceinline__ uint2 run_step(uint2 run, uint2 d)
+{
+    return make_uint2(run.x + (d.x ^ 0x80808080u) + 0x7f7f7f80u,
+                      run.y + (d.y ^ 0x80808080u) + 0x7f7f7f80u);
+}
+
+// a + b per byte, both offset-64: (a + 64) + (b + 64) - 64
+__device__ __forceinline__ uint2 add_off(uint2 a, uint2 b)
+{
+    return make_uint2(a.x + b.x + 0xbfbfbfc0u, a.y + b.y + 0xbfbfbfc0u);
+}
+
+// a - b per byte, both offset-64: ((a + 64) + 64) - (b + 64)
+__device__ __forceinline__ uint2 sub_off(uint2 a, uint2 b)
+{
+    return make_uint2(a.x + kOff64 - b.x, a.y + kOff64 - b.y);
+}
+
 // Decoupled look-back of one tile of a chain, run by the 16 lanes of one lane group (lane g
-// carries group g's 8 running bytes); they move together: a value is taken only when every
-// lane's words are complete. slot: this tile's word slot; the chain's previous tile sits
+// carries group g's 8 running bytes, offset-64); they move together: a value is taken only when
+// every lane's words are complete. slot: this tile's word slot; the chain's previous tile sits
 // `step` slots earlier. Publishes this tile's aggregate (tile > 0) and inclusive prefix, and
 // returns the exclusive prefix. A wait longer than kSpinLimit sets *err and gives up.
 __device__ __forceinline__ uint2 chain_lookback(uint32_t *lb_agg, uint32_t *lb_incl, size_t slot,
                                                 size_t step, int tile, uint2 agg, int g,
                                                 uint32_t *err)
 {
-    uint2 excl = make_uint2(0u, 0u);
+    uint2 excl = make_uint2(kOff64, kOff64);
     const size_t me = (slot * 16 + g) * 4;
     if (tile == 0) {
         lb_publish(lb_incl + me, agg, 2u);
@@ -414,11 +440,11 @@ __device__ __forceinline__ uint2 chain_lookback(uint32_t *lb_agg, uint32_t *lb_i
         const size_t pw = (pred * 16 + g) * 4;
         uint2 v;
         if (__ballot(!lb_read(lb_incl + pw, 2u, v)) == 0ull) {
-            excl = make_uint2(add_bytes(excl.x, v.x), add_bytes(excl.y, v.y));
+            excl = add_off(excl, v);
             break;
         }
         if (__ballot(!lb_read(lb_agg + pw, 1u, v)) == 0ull) {
-            excl = make_uint2(add_bytes(excl.x, v.x), add_bytes(excl.y, v.y));
+            excl = add_off(excl, v);
             pred -= step;
             spins = 0;
             continue;
@@ -429,7 +455,7 @@ __device__ __forceinline__ uint2 chain_lookback(uint32_t *lb_agg, uint32_t *lb_i
         }
         __builtin_amdgcn_s_sleep(1);
     }
-    lb_publish(lb_incl + me, make_uint2(add_bytes(excl.x, agg.x), add_bytes(excl.y, agg.y)), 2u);
+    lb_publish(lb_incl + me, add_off(excl, agg), 2u);
     return excl;
 }
 
@@ -571,26 +597,22 @@ __device__ __forceinline__ void stage_tile(const int8_t *codes, const uint16_t *
 }
 
 // The running code of this lane's group just before lane group q's first token of a staged
-// tile (q walks tile rows q * kDecRun ..), as c + 64 per byte (|c| <= 16 keeps every byte in
-// range, so later steps add whole dwords without carries between bytes). Synchronises the
-// block before reading the tile and after the look-back; slot/step/err as in chain_lookback.
+// tile (q walks tile rows q * kDecRun ..), offset-64 (c + 64 per byte). Synchronises the block
+// before reading the tile and after the look-back; slot/step/err as in chain_lookback.
 __device__ __forceinline__ uint2 tile_run_base(const uint4 *s_delta, int nt, int q, int g,
                                                uint2 (*s_tot)[16], uint2 *s_excl,
                                                uint32_t *lb_agg, uint32_t *lb_incl, size_t slot,
                                                size_t step, int tile, uint32_t *err)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // 1. the byte-wise sum of this lane group's deltas
+    // 1. the sum of this lane group's deltas (offset-64)
     __syncthreads();
     const uint2 *sd = reinterpret_cast<const uint2 *>(s_delta) + g;   // [token][16 lanes]
-    uint2 acc = make_uint2(0u, 0u);
+    uint2 acc = make_uint2(kOff64, kOff64);
 #pragma unroll
     for (int i = 0; i < kDecRun; i++) {
         const int jl = q * kDecRun + i;
-        if (jl < nt) {
-            const uint2 d = sd[jl * 16];
-            acc = make_uint2(add_bytes(acc.x, d.x), add_bytes(acc.y, d.y));
-        }
+        if (jl < nt) acc = run_step(acc, sd[jl * 16]);
     }
     // 2. prefix over the lane groups before this one: across the 4 rows of a wave with lane
     //    shuffles, then across the 4 waves through LDS (one barrier); group 15's lanes then
@@ -601,32 +623,17 @@ __device__ __forceinline__ uint2 tile_run_base(const uint4 *s_delta, int nt, int
     for (int d = 1; d < 4; d <<= 1) {
         const uint2 t = make_uint2((uint32_t)__shfl_up((int)incl.x, 16 * d),
                                    (uint32_t)__shfl_up((int)incl.y, 16 * d));
-        if (row >= d) incl = make_uint2(add_bytes(incl.x, t.x), add_bytes(incl.y, t.y));
+        if (row >= d) incl = add_off(incl, t);
     }
     if (row == 3) s_tot[wave][g] = incl;
     __syncthreads();
-    for (int w = 0; w < wave; w++) {
-        const uint2 t = s_tot[w][g];
-        incl = make_uint2(add_bytes(incl.x, t.x), add_bytes(incl.y, t.y));
-    }
-    const uint2 gp = make_uint2(sub_bytes(incl.x, acc.x), sub_bytes(incl.y, acc.y));
+    for (int w = 0; w < wave; w++) incl = add_off(incl, s_tot[w][g]);
+    const uint2 gp = sub_off(incl, acc);
     // 3. decoupled look-back, done by lane group 15 (it holds the tile total)
     if (q == 15)
-        s_excl[g] = chain_lookback(lb_agg, lb_incl, slot, step, tile,
-                                   make_uint2(add_bytes(gp.x, acc.x), add_bytes(gp.y, acc.y)), g,
-                                   err);
+        s_excl[g] = chain_lookback(lb_agg, lb_incl, slot, step, tile, add_off(gp, acc), g, err);
     __syncthreads();
-    const uint2 base0 = s_excl[g];
-    const uint2 run = make_uint2(add_bytes(base0.x, gp.x), add_bytes(base0.y, gp.y));
-    return make_uint2((run.x ^ 0x80808080u) - 0x40404040u, (run.y ^ 0x80808080u) - 0x40404040u);
-}
-
-// (c + 64) + (d + 128) - 128 per byte, d two's complement with |d| <= 32: every byte stays
-// within [16, 240], so one 32-bit add3 is the byte-wise sum
-__device__ __forceinline__ uint2 run_step(uint2 run, uint2 d)
-{
-    return make_uint2(run.x + (d.x ^ 0x80808080u) + 0x7f7f7f80u,
-                      run.y + (d.y ^ 0x80808080u) + 0x7f7f7f80u);
+    return add_off(s_excl[g], gp);
 }
 
 template <bool IS_KEY>
@@ -654,28 +661,24 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
     const size_t row_off = chain * (size_t)n_keep * kHeadDim;
     const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.scale);
     const int jend = min(n_keep, j0 + kDecRun);
-    float cn[8], sn[8];
+    float rc[2][8], rs[2][8];   // rotary rows of the current and the next token
     if (IS_KEY && j0 < jend) {
         const size_t p = (size_t)s_pos[j0 - t0] * 64 + 8 * (g & 7);
-        load_f32x8(a.rope_cos + p, cn);
-        load_f32x8(a.rope_sin + p, sn);
+        load_f32x8(a.rope_cos + p, rc[0]);
+        load_f32x8(a.rope_sin + p, rs[0]);
     }
 #pragma unroll
     for (int i = 0; i < kDecRun; i++) {
-        const int j = j0 + i;
+        const int j = j0 + i, cur = i & 1;
         if (j < jend) {
-            float cr[8], sr[8];
-            if (IS_KEY) {
-#pragma unroll
-                for (int k = 0; k < 8; k++) { cr[k] = cn[k]; sr[k] = sn[k]; }
-                if (j + 1 < jend) {
-                    const size_t p = (size_t)s_pos[j + 1 - t0] * 64 + 8 * (g & 7);
-                    load_f32x8(a.rope_cos + p, cn);
-                    load_f32x8(a.rope_sin + p, sn);
-                }
+            if (IS_KEY && j + 1 < jend) {
+                const size_t p = (size_t)s_pos[j + 1 - t0] * 64 + 8 * (g & 7);
+                load_f32x8(a.rope_cos + p, rc[cur ^ 1]);
+                load_f32x8(a.rope_sin + p, rs[cur ^ 1]);
             }
             run = run_step(run, sd[(j - t0) * 16]);
-            decode_store<IS_KEY>(a, row_off, j, g, run, sl[(j - t0) * kGroups + g], cr, sr);
+            decode_store<IS_KEY>(a, row_off, j, g, run, sl[(j - t0) * kGroups + g], rc[cur],
+                                 rs[cur]);
         }
     }
 }

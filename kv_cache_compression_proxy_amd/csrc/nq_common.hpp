@@ -81,18 +81,6 @@ __device__ __forceinline__ float dpp(float v)
 
 __device__ __forceinline__ float lane_xor8(float v) { return dpp<kDppRor8>(v); }
 
-// Byte-wise (mod 256) addition of four packed bytes, no carries between bytes.
-__device__ __forceinline__ uint32_t add_bytes(uint32_t a, uint32_t b)
-{
-    return ((a & 0x7f7f7f7fu) + (b & 0x7f7f7f7fu)) ^ ((a ^ b) & 0x80808080u);
-}
-
-// Byte-wise (mod 256) subtraction a - b.
-__device__ __forceinline__ uint32_t sub_bytes(uint32_t a, uint32_t b)
-{
-    return ((a | 0x80808080u) - (b & 0x7f7f7f7fu)) ^ ((a ^ ~b) & 0x80808080u);
-}
-
 // Workgroup-to-XCD aware block order. The dispatcher hands consecutive workgroup ids to the 8
 // XCDs round robin; this maps the hardware id to a logical id so that logically consecutive
 // blocks (which share cached rows, e.g. the rotary table of one token tile) run on one XCD and

@@ -48,15 +48,72 @@ struct FusedShared {
     } u;
 };
 
-// sum over the 16 lanes of a row (every lane gets the sum); xor partners 1, 2, 7, 8 generate
-// all 16 lanes
-__device__ __forceinline__ float row_sum16(float v)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
 {
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kDppRor8, 0xF, 0xF, true));
-    return v;
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// One transpose-reduce level across lane partners l ^ m (DPP control CTRL): lanes whose
+// selecting bit is clear keep a + a(partner), the others b + b(partner).
+template <int CTRL>
+__device__ __forceinline__ float tr_level(float a, float b, bool hi)
+{
+    return (hi ? b : a) + dpp_f<CTRL>(hi ? a : b);
+}
+
+// Sums of G per-lane values d[0..G) over the 16 lanes of a row. Transpose-reduce: the levels
+// run over lane partners l ^ 8, l ^ 7, l ^ 2, l ^ 1 (row_ror:8, row_half_mirror, quad_perm);
+// while more than one value is live, each level halves them, keeping in every lane the half
+// picked by one bit of l (bits 3, 2, 1), so all levels together cost G - 1 + log2(16 / G)
+// adds instead of 4 G. Returns the sum of value row_sum_index<G>(l) for this lane l.
+template <int G>
+__device__ __forceinline__ float row_sums(const float (&d)[G], int l)
+{
+    constexpr int kRor8 = kDppRor8, kHm = 0x141, kX2 = 0x4E, kX1 = 0xB1;
+    const bool b3 = l & 8, b2 = l & 4, b1 = l & 2;
+    if constexpr (G == 1) {
+        float v = d[0] + dpp_f<kRor8>(d[0]);
+        v += dpp_f<kHm>(v);
+        v += dpp_f<kX2>(v);
+        return v + dpp_f<kX1>(v);
+    } else if constexpr (G == 2) {
+        float v = tr_level<kRor8>(d[0], d[1], b3);
+        v += dpp_f<kHm>(v);
+        v += dpp_f<kX2>(v);
+        return v + dpp_f<kX1>(v);
+    } else if constexpr (G == 4) {
+        const float v01 = tr_level<kRor8>(d[0], d[1], b3);
+        const float v23 = tr_level<kRor8>(d[2], d[3], b3);
+        float v = tr_level<kHm>(v01, v23, b2);
+        v += dpp_f<kX2>(v);
+        return v + dpp_f<kX1>(v);
+    } else {
+        static_assert(G == 8, "G in {1, 2, 4, 8}");
+        const float v01 = tr_level<kRor8>(d[0], d[1], b3);
+        const float v23 = tr_level<kRor8>(d[2], d[3], b3);
+        const float v45 = tr_level<kRor8>(d[4], d[5], b3);
+        const float v67 = tr_level<kRor8>(d[6], d[7], b3);
+        const float v03 = tr_level<kHm>(v01, v23, b2);
+        const float v47 = tr_level<kHm>(v45, v67, b2);
+        const float v = tr_level<kX2>(v03, v47, b1);
+        return v + dpp_f<kX1>(v);
+    }
+}
+
+// which value row_sums<G> leaves in lane l (0..15), and whether lane l is the one that
+// reports it (one lane per value)
+template <int G>
+__device__ __forceinline__ int row_sum_index(int l)
+{
+    return (G >= 2 ? (l >> 3) & 1 : 0) | (G >= 4 ? ((l >> 2) & 1) << 1 : 0) |
+           (G >= 8 ? ((l >> 1) & 1) << 2 : 0);
+}
+
+template <int G>
+__device__ __forceinline__ bool row_sum_reporter(int l)
+{
+    return (l & (G == 1 ? 15 : G == 2 ? 7 : G == 4 ? 3 : 1)) == 0;
 }
 
 // grid: pairs * tiles blocks (pairs = Lc * H); tickets tile-major over the pairs as in
@@ -104,35 +161,33 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
         const uint2 *sd = reinterpret_cast<const uint2 *>(sh.u.t.delta) + g;
         const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.u.t.scale);
         const int jend = min(nt, jl0 + kDecRun);
-        float cn[8], sn[8];
+        float rc[2][8], rs[2][8];   // rotary rows of the current and the next token
         if (jl0 < jend) {
             const size_t p = (size_t)sh.pos[jl0] * 64 + 8 * (g & 7);
-            load_f32x8(a.rope_cos + p, cn);
-            load_f32x8(a.rope_sin + p, sn);
+            load_f32x8(a.rope_cos + p, rc[0]);
+            load_f32x8(a.rope_sin + p, rs[0]);
         }
 #pragma unroll
         for (int i = 0; i < kDecRun; i++) {
-            const int jl = jl0 + i;
+            const int jl = jl0 + i, cur = i & 1;
             if (jl < jend) {
-                float cr[8], sr[8];
-#pragma unroll
-                for (int k = 0; k < 8; k++) { cr[k] = cn[k]; sr[k] = sn[k]; }
                 if (jl + 1 < jend) {
                     const size_t p = (size_t)sh.pos[jl + 1] * 64 + 8 * (g & 7);
-                    load_f32x8(a.rope_cos + p, cn);
-                    load_f32x8(a.rope_sin + p, sn);
+                    load_f32x8(a.rope_cos + p, rc[cur ^ 1]);
+                    load_f32x8(a.rope_sin + p, rs[cur ^ 1]);
                 }
                 run = run_step(run, sd[jl * 16]);
                 float x[8];
-                decode_row<true>(g, run, sl[jl * kGroups + g], cr, sr, x);
+                decode_row<true>(g, run, sl[jl * kGroups + g], rc[cur], rs[cur], x);
+                float d[G];
 #pragma unroll
                 for (int hq = 0; hq < G; hq++) {
-                    float d = 0.0f;
+                    d[hq] = 0.0f;
 #pragma unroll
-                    for (int k = 0; k < 8; k++) d = __builtin_fmaf(qv[hq][k], x[k], d);
-                    d = row_sum16(d);
-                    if ((lane & 15) == 0) sh.z[jl][hq] = d;
+                    for (int k = 0; k < 8; k++) d[hq] = __builtin_fmaf(qv[hq][k], x[k], d[hq]);
                 }
+                const float z = row_sums<G>(d, lane & 15);
+                if (row_sum_reporter<G>(lane & 15)) sh.z[jl][row_sum_index<G>(lane & 15)] = z;
             }
         }
     }
