@@ -155,7 +155,7 @@ FusedWs fused_ws(const nq_params *p, int32_t q_heads, void *base)
 {
     FusedWs w;
     w.pairs = compressed_layers(p) * p->kv_heads;
-    w.tiles = decode_tiles(p);
+    w.tiles = (keep_count(p) + nq::kFusedTile - 1) / nq::kFusedTile;
     const size_t G = (size_t)(q_heads / p->kv_heads);
     const size_t words = (size_t)w.pairs * w.tiles * 2 * 16 * 4;
     const size_t t = align_up(2 * sizeof(uint32_t));

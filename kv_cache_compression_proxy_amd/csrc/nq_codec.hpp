@@ -566,39 +566,48 @@ struct DecodeShared {
     uint4 delta[kDecTile * kHeadDim / 16];        // the tile's delta codes
 };
 
-// Loads a tile of one chain into LDS: nt (<= kDecTile) rows of delta codes and scales starting
+// Loads a tile of one chain into LDS: nt (<= 16 * RUN) rows of delta codes and scales starting
 // at chain row `row0`, and, when pos is not null, the nt positions (clamped into [0, T)). Every
 // load of a thread is issued before its first LDS store, so they are in flight together (one
 // memory latency per tile, not one per chunk). The caller synchronises before reading.
+template <int RUN>
 __device__ __forceinline__ void stage_tile(const int8_t *codes, const uint16_t *scales,
                                            size_t row0, int nt, const int32_t *pos, int T,
                                            uint4 *s_delta, uint4 *s_scale, int32_t *s_pos)
 {
-    constexpr int kDeltaChunks = kDecTile * kHeadDim / 16 / kCodecThreads;
-    static_assert(kDecTile * kGroups * 2 / 16 <= kCodecThreads && kDecTile <= kCodecThreads,
-                  "one scale chunk and one position per thread");
+    constexpr int kTile = 16 * RUN;
+    constexpr int kDeltaChunks = kTile * kHeadDim / 16 / kCodecThreads;
+    constexpr int kScaleChunks = (kTile * 2 + kCodecThreads - 1) / kCodecThreads;
+    static_assert(kTile <= kCodecThreads, "one position per thread");
     const u32x4 *dc = reinterpret_cast<const u32x4 *>(codes + row0 * kHeadDim);
     const u32x4 *sc = reinterpret_cast<const u32x4 *>(scales + row0 * kGroups);
     const int tid = threadIdx.x;
-    u32x4 d[kDeltaChunks], sv = {0u, 0u, 0u, 0u};
+    u32x4 d[kDeltaChunks], sv[kScaleChunks];
     int pv = 0;
 #pragma unroll
     for (int k = 0; k < kDeltaChunks; k++)
         if (tid + k * kCodecThreads < 8 * nt)
             d[k] = __builtin_nontemporal_load(dc + tid + k * kCodecThreads);
-    if (tid < 2 * nt) sv = __builtin_nontemporal_load(sc + tid);
+#pragma unroll
+    for (int k = 0; k < kScaleChunks; k++)
+        if (tid + k * kCodecThreads < 2 * nt)
+            sv[k] = __builtin_nontemporal_load(sc + tid + k * kCodecThreads);
     if (pos && tid < nt) pv = pos[tid];
 #pragma unroll
     for (int k = 0; k < kDeltaChunks; k++)
         if (tid + k * kCodecThreads < 8 * nt)
             s_delta[tid + k * kCodecThreads] = make_uint4(d[k].x, d[k].y, d[k].z, d[k].w);
-    if (tid < 2 * nt) s_scale[tid] = make_uint4(sv.x, sv.y, sv.z, sv.w);
+#pragma unroll
+    for (int k = 0; k < kScaleChunks; k++)
+        if (tid + k * kCodecThreads < 2 * nt)
+            s_scale[tid + k * kCodecThreads] = make_uint4(sv[k].x, sv[k].y, sv[k].z, sv[k].w);
     if (pos && tid < nt) s_pos[tid] = min(max(pv, 0), T - 1);
 }
 
 // The running code of this lane's group just before lane group q's first token of a staged
-// tile (q walks tile rows q * kDecRun ..), offset-64 (c + 64 per byte). Synchronises the block
+// tile (q walks tile rows q * RUN ..), offset-64 (c + 64 per byte). Synchronises the block
 // before reading the tile and after the look-back; slot/step/err as in chain_lookback.
+template <int RUN>
 __device__ __forceinline__ uint2 tile_run_base(const uint4 *s_delta, int nt, int q, int g,
                                                uint2 (*s_tot)[16], uint2 *s_excl,
                                                uint32_t *lb_agg, uint32_t *lb_incl, size_t slot,
@@ -610,8 +619,8 @@ __device__ __forceinline__ uint2 tile_run_base(const uint4 *s_delta, int nt, int
     const uint2 *sd = reinterpret_cast<const uint2 *>(s_delta) + g;   // [token][16 lanes]
     uint2 acc = make_uint2(kOff64, kOff64);
 #pragma unroll
-    for (int i = 0; i < kDecRun; i++) {
-        const int jl = q * kDecRun + i;
+    for (int i = 0; i < RUN; i++) {
+        const int jl = q * RUN + i;
         if (jl < nt) acc = run_step(acc, sd[jl * 16]);
     }
     // 2. prefix over the lane groups before this one: across the 4 rows of a wave with lane
@@ -649,11 +658,11 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
     const int j0 = t0 + q * kDecRun;
     const int32_t *s_pos = sh.pos;
 
-    stage_tile(IS_KEY ? a.codes_k : a.codes_v, IS_KEY ? a.scales_k : a.scales_v,
+    stage_tile<kDecRun>(IS_KEY ? a.codes_k : a.codes_v, IS_KEY ? a.scales_k : a.scales_v,
                chain * (size_t)n_keep + t0, nt,
                IS_KEY ? a.positions + (size_t)lc * n_keep + t0 : nullptr, a.T, sh.delta,
                sh.scale, sh.pos);
-    uint2 run = tile_run_base(sh.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
+    uint2 run = tile_run_base<kDecRun>(sh.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
                               (size_t)ticket, (size_t)chains, tile, a.lb_ticket + 1);
     const uint2 *sd = reinterpret_cast<const uint2 *>(sh.delta) + g;   // [token][16 lanes]
     // 4. reconstruct every token of this lane group; the next token's rotary rows are requested

@@ -3,7 +3,7 @@
 // (the VQKV page, "推理流程集成": reconstruct on demand while decoding, attending over the
 // reconstructed cache).
 //
-// A block owns one tile of kDecTile kept tokens of one (layer, kv head) pair and the G query
+// A block owns one tile of kFusedTile kept tokens of one (layer, kv head) pair and the G query
 // heads that share that kv head. Keys: the K chain's running codes come from the same staged
 // scan and decoupled look-back as nq_decode; each key row is rebuilt in registers (inverse
 // Hadamard, RoPE at its position) and dotted with the G queries. Values: because
@@ -31,18 +31,20 @@ struct FusedArgs {
 
 // a tile partial per query head: running max, sum of weights, then 128 accumulated dims
 constexpr int kPartStride = 2 + kHeadDim;
+constexpr int kFusedRun = 16;                  // tokens per lane group
+constexpr int kFusedTile = 16 * kFusedRun;     // tokens per block
 
 template <int G>
 struct FusedShared {
     uint2 tot[4][16];
     uint2 excl[16];
-    int32_t pos[kDecTile];
-    float z[kDecTile][G];   // scores, then weights exp(z - m)
+    int32_t pos[kFusedTile];
+    float z[kFusedTile][G];   // scores, then weights exp(z - m)
     float ml[G][2];         // the tile's max and sum per query head
     union {
         struct {
-            uint4 scale[kDecTile * kGroups * 2 / 16];
-            uint4 delta[kDecTile * kHeadDim / 16];
+            uint4 scale[kFusedTile * kGroups * 2 / 16];
+            uint4 delta[kFusedTile * kHeadDim / 16];
         } t;
         float red[4][G][16][9];   // per-wave sums of the value accumulators
     } u;
@@ -134,9 +136,9 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane_group(lane & 15), q = wave * 4 + (lane >> 4);
     const int n_keep = a.n_keep;
-    const int t0 = tile * kDecTile;
-    const int nt = min(kDecTile, n_keep - t0);
-    const int jl0 = q * kDecRun;                       // this lane group's first tile row
+    const int t0 = tile * kFusedTile;
+    const int nt = min(kFusedTile, n_keep - t0);
+    const int jl0 = q * kFusedRun;                     // this lane group's first tile row
     const size_t row0 = (size_t)pair * n_keep + t0;    // chain row of the tile's first token
 
     // queries of this kv head, this lane's 8 dims, times group_sign(g) / sqrt(128): the keys
@@ -153,14 +155,14 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
     }
 
     // ---- keys: scores z[t][i] of the tile
-    stage_tile(a.codes_k, a.scales_k, row0, nt, a.positions + (size_t)lc * n_keep + t0, a.T,
+    stage_tile<kFusedRun>(a.codes_k, a.scales_k, row0, nt, a.positions + (size_t)lc * n_keep + t0, a.T,
                sh.u.t.delta, sh.u.t.scale, sh.pos);
     {
-        uint2 run = tile_run_base(sh.u.t.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
+        uint2 run = tile_run_base<kFusedRun>(sh.u.t.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
                                   2 * (size_t)ticket, 2 * (size_t)pairs, tile, a.lb_ticket + 1);
         const uint2 *sd = reinterpret_cast<const uint2 *>(sh.u.t.delta) + g;
         const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.u.t.scale);
-        const int jend = min(nt, jl0 + kDecRun);
+        const int jend = min(nt, jl0 + kFusedRun);
         float rc[2][8], rs[2][8];   // rotary rows of the current and the next token
         if (jl0 < jend) {
             const size_t p = (size_t)sh.pos[jl0] * 64 + 8 * (g & 7);
@@ -168,7 +170,7 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
             load_f32x8(a.rope_sin + p, rs[0]);
         }
 #pragma unroll
-        for (int i = 0; i < kDecRun; i++) {
+        for (int i = 0; i < kFusedRun; i++) {
             const int jl = jl0 + i, cur = i & 1;
             if (jl < jend) {
                 if (jl + 1 < jend) {
@@ -193,26 +195,34 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
     }
     __syncthreads();
 
-    // ---- softmax within the tile: wave w handles query heads w, w + 4, ...; 2 rows per lane
+    // ---- softmax within the tile: wave w handles query heads w, w + 4, ...; kFusedTile / 64
+    //      rows per lane
+    constexpr int kRows = kFusedTile / 64;
     for (int hq = wave; hq < G; hq += 4) {
-        const float z0 = lane < nt ? sh.z[lane][hq] : -INFINITY;
-        const float z1 = lane + 64 < nt ? sh.z[lane + 64][hq] : -INFINITY;
-        float m = fmaxf(z0, z1);
+        float zr[kRows];
+        float m = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < kRows; r++) {
+            zr[r] = lane + 64 * r < nt ? sh.z[lane + 64 * r][hq] : -INFINITY;
+            m = fmaxf(m, zr[r]);
+        }
 #pragma unroll
         for (int msk = 1; msk < 64; msk <<= 1) m = fmaxf(m, __shfl_xor(m, msk));
-        const float p0 = lane < nt ? expf(z0 - m) : 0.0f;
-        const float p1 = lane + 64 < nt ? expf(z1 - m) : 0.0f;
-        float l = p0 + p1;
+        float l = 0.0f;
+#pragma unroll
+        for (int r = 0; r < kRows; r++) {
+            const float pr = lane + 64 * r < nt ? expf(zr[r] - m) : 0.0f;
+            if (lane + 64 * r < nt) sh.z[lane + 64 * r][hq] = pr;
+            l += pr;
+        }
 #pragma unroll
         for (int msk = 1; msk < 64; msk <<= 1) l += __shfl_xor(l, msk);
-        if (lane < nt) sh.z[lane][hq] = p0;
-        if (lane + 64 < nt) sh.z[lane + 64][hq] = p1;
         if (lane == 0) { sh.ml[hq][0] = m; sh.ml[hq][1] = l; }
     }
     __syncthreads();   // also: every key row has been read, the staging area may be reused
 
     // ---- values: acc[i][k] = sum_t p_t,i * (s_t / 2) * (c_t,k + 64), W[i] = sum_t p_t,i s_t / 2
-    stage_tile(a.codes_v, a.scales_v, row0, nt, nullptr, a.T, sh.u.t.delta, sh.u.t.scale,
+    stage_tile<kFusedRun>(a.codes_v, a.scales_v, row0, nt, nullptr, a.T, sh.u.t.delta, sh.u.t.scale,
                nullptr);
     float acc[G][8], W[G];
 #pragma unroll
@@ -222,14 +232,14 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
         for (int k = 0; k < 8; k++) acc[i][k] = 0.0f;
     }
     {
-        uint2 run = tile_run_base(sh.u.t.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
+        uint2 run = tile_run_base<kFusedRun>(sh.u.t.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
                                   2 * (size_t)ticket + 1, 2 * (size_t)pairs, tile,
                                   a.lb_ticket + 1);
         const uint2 *sd = reinterpret_cast<const uint2 *>(sh.u.t.delta) + g;
         const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.u.t.scale);
-        const int jend = min(nt, jl0 + kDecRun);
+        const int jend = min(nt, jl0 + kFusedRun);
 #pragma unroll
-        for (int i = 0; i < kDecRun; i++) {
+        for (int i = 0; i < kFusedRun; i++) {
             const int jl = jl0 + i;
             if (jl < jend) {
                 run = run_step(run, sd[jl * 16]);
