@@ -23,6 +23,9 @@ Recipe (all in numpy, layer by layer, so any one layer can be rebuilt alone):
     k_i = x_i*cos - x_{i+64}*sin, k_{i+64} = x_{i+64}*cos + x_i*sin, in float32 with
     cos/sin rounded from float64 angles; then both tensors are rounded to float16.
   * single-token decode queries: ``default_rng([seed, 99]).standard_normal`` -> float16.
+  * observation-window queries (the attention scorer's stand-in for a model's last W query
+    rows): ``default_rng([seed, layer, 2]).standard_normal((Hq, W, 128), float32)``, given the
+    same forward rotary embedding at positions T - W .. T - 1, then float16.
 """
 from __future__ import annotations
 
@@ -158,3 +161,26 @@ def queries(w: Workload, q_heads: int | None = None) -> np.ndarray:
     rng = np.random.default_rng([w.seed, 99])
     return rng.standard_normal((w.compressed_layers, hq, HEAD_DIM),
                                dtype=np.float32).astype(np.float16)
+
+
+def window_queries(w: Workload, layer: int, q_heads: int | None = None,
+                   tokens: int | None = None) -> np.ndarray:
+    """float16 queries [q_heads, W, 128] of one layer's observation window: query w sits at
+    position T - W + w and carries the forward rotary embedding of that position (positions
+    below 0, when W > T, are left unrotated; the scorer ignores those rows)."""
+    T = w.tokens if tokens is None else tokens
+    hq = q_heads or w.q_heads or 4 * w.kv_heads
+    W = w.window
+    x = np.random.default_rng([w.seed, layer, 2]).standard_normal((hq, W, HEAD_DIM),
+                                                                   dtype=np.float32)
+    c, s = _rope_cos_sin(max(T, 1), w.rope_base)
+    pos = T - W + np.arange(W)
+    ok = pos >= 0
+    cc = np.ones((W, 64), np.float32)
+    ss = np.zeros((W, 64), np.float32)
+    cc[ok], ss[ok] = c[pos[ok]], s[pos[ok]]
+    out = np.empty(x.shape, dtype=np.float16)
+    lo, hi = x[..., :64], x[..., 64:]
+    out[..., :64] = (lo * cc - hi * ss).astype(np.float16)
+    out[..., 64:] = (hi * cc + lo * ss).astype(np.float16)
+    return out
