@@ -52,6 +52,10 @@ def parse():
                          "and exit")
     ap.add_argument("--pmc-command", default="",
                     help="the profiling command, recorded in the summary")
+    ap.add_argument("--attn-score", action="store_true",
+                    help="time the attention-weight scorer (nq_score_evict_attn, 32 query heads, "
+                         "W-query observation window) against the key-key proxy scorer on the "
+                         "headline workload instead")
     ap.add_argument("--decode-step", action="store_true",
                     help="time the one-token GQA decode step over the long-context compressed "
                          "cache instead: fused nq_decode_attend against nq_decode + "
@@ -225,6 +229,83 @@ def upload_workload(w, dev):
     return K, V
 
 
+def attn_score(args):
+    """The attention-weight scorer on the headline workload: 32 query heads (GQA 4) with a
+    W-query observation window per head, two matrix-core passes over all keys, then the
+    selection -- timed against the key-key proxy scorer on the same keys."""
+    import torch
+    import kv_cache_compression_proxy_amd as nq
+    import kvsynth
+    w = kvsynth.workload(args.workload)
+    p = nq.make_params(w.layers, w.kv_heads, w.tokens, w.window, w.evict_permille, w.bits_k,
+                       w.bits_v, w.rope_base, w.layer_begin, w.layer_end)
+    Lc, H, T, W = w.compressed_layers, w.kv_heads, w.tokens, w.window
+    Hq = 4 * H
+    n = nq.nq_keep_count(p)
+    dev = torch.device("cuda:0")
+    log(f"[attn-score] workload {w.name}: Lc={Lc} H={H} Hq={Hq} T={T} W={W} n_keep={n}")
+    K, V = upload_workload(w, dev)
+    del V
+    Qs = np.stack([kvsynth.window_queries(w, w.layer_begin + lc, q_heads=Hq) for lc in range(Lc)])
+    Q = torch.from_numpy(Qs).to(dev)
+    pos_a = torch.empty((Lc, n), dtype=torch.int32, device=dev)
+    pos_k = torch.empty_like(pos_a)
+    ws_a = nq.workspace(nq.nq_score_evict_attn_workspace_bytes(p, Hq), dev)
+    ws_k = nq.workspace(nq.nq_score_evict_workspace_bytes(p), dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms_a = timed(lambda: nq.nq_score_evict_attn(p, K, Q, Hq, pos_a, ws_a, stream=stream))
+    ms_k = timed(lambda: nq.nq_score_evict(p, K, pos_k, ws_k, stream=stream))
+    same = int((pos_a == pos_k).all(dim=1).sum().item())
+    overlap = float(np.mean([len(set(pos_a[l].tolist()) & set(pos_k[l].tolist())) / n
+                             for l in range(Lc)]))
+    # two matrix-core passes over every (query row, key) pair of each (layer, kv head):
+    # pass 1 over keys up to each row block's last position, pass 2 over the candidates
+    R, c_end = 4 * W, T - W
+    flop = 2.0 * Lc * H * R * 128 * (T + c_end)
+    exps = 1.0 * Lc * H * R * (T + c_end)
+    tflops = flop / (ms_a * 1e-3) / 1e12
+    log(f"[attn-score] {ms_a:.3f} ms (key-key proxy {ms_k:.3f} ms); {tflops:.1f} TFLOP/s; "
+        f"keep-set overlap with the proxy {overlap:.3f}")
+    res = {
+        "metric": "attention-weight scorer: candidate scores + eviction per step",
+        "value": round(Lc * H * T * 256 / (ms_a * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_a, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 products, f32 sums",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": Lc, "kv_heads": H, "q_heads": Hq,
+                   "tokens": T, "window": W, "n_keep": n, "parallelism": "none (1 GPU)"},
+        "key_key_proxy_ms": round(ms_k, 4),
+        "keep_overlap_with_proxy": round(overlap, 4),
+        "layers_with_identical_keep_sets": same,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0,
+                     "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "kernel": "k_attn_rowbias+k_attn_colsum+k_attn_finish+k_select",
+                     "algorithmic_flop_per_launch": flop, "exp2_per_launch": exps,
+                     "avg_launch_ms": round(ms_a, 4)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def decode_step(args):
     """One-token GQA decode step over the long-context compressed cache (32 query heads over 8
     kv heads, one fp16 query per layer): the fused nq_decode_attend against the two-call path
@@ -344,6 +425,9 @@ def main():
         return
     if args.decode_step:
         decode_step(args)
+        return
+    if args.attn_score:
+        attn_score(args)
         return
     import torch
     import kv_cache_compression_proxy_amd as nq

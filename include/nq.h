@@ -103,6 +103,29 @@ nq_status nq_rope_table(const nq_params *p, float *cos_dev, float *sin_dev, void
 nq_status nq_score_evict(const nq_params *p, const void *K, int32_t *positions,
                          double *scores_opt, void *workspace, size_t ws_bytes, void *stream);
 
+/* Device workspace needed by nq_score_evict_attn for q_heads query heads (bytes). 0 if p is
+ * invalid. */
+size_t nq_score_evict_attn_workspace_bytes(const nq_params *p, int32_t q_heads);
+
+/* Steps 1-2 with the attention-weight scorer ("技术实现细节": the real attention scorer,
+ * higher quality at the cost of an extra pass; "Token淘汰机制": tokens ranked by their attention
+ * weights, BOS and the recent window always kept). Per compressed layer, an observation window
+ * of W = window queries per query head (query w at position T - W + w; positions below 0 are
+ * ignored) scores each candidate t in [1, T - W) by
+ *   s_t = sum_j sum_w softmax_{t' <= T-W+w}(<q_{j,w}, k_{j/G,t'}> / sqrt(128))_t,
+ * G = q_heads / H, over the stored (rotary-embedded) keys; fp16 products, fp32 sums and
+ * softmax, fp64 sum over kv heads. The selection is the one of nq_score_evict.
+ *   K          fp16 [L][H][T][128]
+ *   Q_obs      fp16 [layer_end-layer_begin][q_heads][window][128], used as given (already
+ *              rotary-embedded for their positions); q_heads a positive multiple of H
+ *   positions  int32 [layer_end-layer_begin][n_keep] out: kept positions, ascending
+ *   scores_opt NULL, or fp64 [layer_end-layer_begin][T] out: s_t for t in [0, T - W) (other
+ *              entries are not written)
+ *   workspace  device scratch of nq_score_evict_attn_workspace_bytes(p, q_heads) bytes */
+nq_status nq_score_evict_attn(const nq_params *p, const void *K, const void *Q_obs,
+                              int32_t q_heads, int32_t *positions, double *scores_opt,
+                              void *workspace, size_t ws_bytes, void *stream);
+
 /* Steps 3-6: RoPE removal, Hadamard rotation, E8 quantization, delta coding ("Como funciona"
  * steps 3-6; "E8格点量化"). For every compressed layer, kv head and kept position p (in the
  * order given): keys are rotated back by -p (split-half pairs (i, i+64)); keys and values get

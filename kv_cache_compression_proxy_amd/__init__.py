@@ -34,7 +34,8 @@ NQ_OUT_F16, NQ_OUT_F32 = 0, 1
 EXPORTED = ("nq_keep_count", "nq_check_params", "nq_score_evict_workspace_bytes",
             "nq_decode_workspace_bytes", "nq_attend_workspace_bytes", "nq_rope_table",
             "nq_score_evict", "nq_encode", "nq_decode", "nq_attend_decode",
-            "nq_decode_attend_workspace_bytes", "nq_decode_attend", "nq_status_string")
+            "nq_decode_attend_workspace_bytes", "nq_decode_attend",
+            "nq_score_evict_attn_workspace_bytes", "nq_score_evict_attn", "nq_status_string")
 
 
 class NqParams(C.Structure):
@@ -64,6 +65,8 @@ _sig = {
     "nq_decode_attend_workspace_bytes": (C.c_size_t, [_P, C.c_int32]),
     "nq_decode_attend": (C.c_int, [_P, _v, _v, _v, _v, _v, _v, _v, _v, C.c_int32, _v, _v,
                                    C.c_size_t, _v]),
+    "nq_score_evict_attn_workspace_bytes": (C.c_size_t, [_P, C.c_int32]),
+    "nq_score_evict_attn": (C.c_int, [_P, _v, _v, C.c_int32, _v, _v, _v, C.c_size_t, _v]),
     "nq_status_string": (C.c_char_p, [C.c_int]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -160,6 +163,17 @@ def nq_attend_decode(p, Q, q_heads, K, V, n_tok, out, workspace, stream=None):
                                                   _stream(stream)))
 
 
+def nq_score_evict_attn_workspace_bytes(p: NqParams, q_heads: int) -> int:
+    return _lib.nq_score_evict_attn_workspace_bytes(C.byref(p), q_heads)
+
+
+def nq_score_evict_attn(p, K, Q_obs, q_heads, positions, workspace, scores=None, stream=None):
+    ws = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _ok("nq_score_evict_attn", _lib.nq_score_evict_attn(
+        C.byref(p), _ptr(K), _ptr(Q_obs), q_heads, _ptr(positions), _ptr(scores),
+        _ptr(workspace), ws, _stream(stream)))
+
+
 def nq_decode_attend_workspace_bytes(p: NqParams, q_heads: int) -> int:
     return _lib.nq_decode_attend_workspace_bytes(C.byref(p), q_heads)
 
@@ -207,8 +221,11 @@ def rope_table(p: NqParams, device="cuda", stream=None):
     return cos, sin
 
 
-def compress(K, V, preset: str = "balanced", rope=None, stream=None, **overrides) -> Compressed:
-    """K, V: fp16 CUDA tensors [L, H, T, 128]. Runs scoring + eviction + encode on the GPU."""
+def compress(K, V, preset: str = "balanced", rope=None, stream=None, window_queries=None,
+             **overrides) -> Compressed:
+    """K, V: fp16 CUDA tensors [L, H, T, 128]. Runs scoring + eviction + encode on the GPU.
+    window_queries: None for the key-key proxy scorer, or fp16 [Lc, Hq, window, 128] queries of
+    the observation window for the attention-weight scorer."""
     import torch
     L, H, T, D = K.shape
     p = params_for(preset, L, H, T, **overrides)
@@ -218,8 +235,13 @@ def compress(K, V, preset: str = "balanced", rope=None, stream=None, **overrides
     dev = K.device
     cos, sin = rope if rope is not None else rope_table(p, dev, stream)
     positions = torch.empty((Lc, n_keep), dtype=torch.int32, device=dev)
-    ws = workspace(nq_score_evict_workspace_bytes(p), dev)
-    nq_score_evict(p, K, positions, ws, stream=stream)
+    if window_queries is None:
+        ws = workspace(nq_score_evict_workspace_bytes(p), dev)
+        nq_score_evict(p, K, positions, ws, stream=stream)
+    else:
+        hq = window_queries.shape[1]
+        ws = workspace(nq_score_evict_attn_workspace_bytes(p, hq), dev)
+        nq_score_evict_attn(p, K, window_queries, hq, positions, ws, stream=stream)
     ck = torch.empty((Lc, H, n_keep, 128), dtype=torch.int8, device=dev)
     cv = torch.empty_like(ck)
     sk = torch.empty((Lc, H, n_keep, 16), dtype=torch.float16, device=dev)

@@ -10,6 +10,7 @@
 
 #include "nq.h"
 #include "nq_attend.hpp"
+#include "nq_attn_score.hpp"
 #include "nq_codec.hpp"
 #include "nq_fused.hpp"
 #include "nq_score.hpp"
@@ -170,6 +171,27 @@ FusedWs fused_ws(const nq_params *p, int32_t q_heads, void *base)
     return w;
 }
 
+struct AttnScoreWs {
+    float *bias, *colsum;
+    double *scores;
+    size_t bytes;
+};
+
+AttnScoreWs attn_score_ws(const nq_params *p, int32_t q_heads, void *base)
+{
+    const size_t pairs = (size_t)compressed_layers(p) * p->kv_heads;
+    const size_t R = (size_t)(q_heads / p->kv_heads) * p->window;
+    const size_t b = align_up(pairs * R * sizeof(float));
+    const size_t c = align_up(pairs * (size_t)p->tokens * sizeof(float));
+    const size_t d = align_up((size_t)compressed_layers(p) * p->tokens * sizeof(double));
+    AttnScoreWs w;
+    w.bias = (float *)base;
+    w.colsum = (float *)((char *)base + b);
+    w.scores = (double *)((char *)base + b + c);
+    w.bytes = b + c + d;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -253,6 +275,63 @@ nq_status nq_score_evict(const nq_params *p, const void *K, int32_t *positions,
     hipLaunchKernelGGL(nq::k_select, dim3(Lc), dim3(nq::kSelThreads), 0, s, scores, T,
                        p->window, n_keep, positions);
     return launched("nq_score_evict");
+}
+
+size_t nq_score_evict_attn_workspace_bytes(const nq_params *p, int32_t q_heads)
+{
+    if (check(p) != NQ_OK || q_heads < 1 || q_heads % p->kv_heads) return 0;
+    return attn_score_ws(p, q_heads, nullptr).bytes;
+}
+
+nq_status nq_score_evict_attn(const nq_params *p, const void *K, const void *Q_obs,
+                              int32_t q_heads, int32_t *positions, double *scores_opt,
+                              void *workspace, size_t ws_bytes, void *stream)
+{
+    nq_status st = check(p);
+    if (st != NQ_OK) return st;
+    if (q_heads < 1 || q_heads % p->kv_heads) return NQ_ERR_INVALID_ARG;
+    const int32_t Lc = compressed_layers(p), T = p->tokens, H = p->kv_heads, W = p->window;
+    const int32_t G = q_heads / H, n_keep = keep_count(p);
+    if ((int64_t)G * W > INT32_MAX / 2) return NQ_ERR_UNSUPPORTED;
+    if (Lc == 0 || T == 0) return NQ_OK;
+    if (!K || !positions || !aligned(K, 16) || !aligned(positions, 4)) return NQ_ERR_INVALID_ARG;
+    if (W > 0 && (!Q_obs || !aligned(Q_obs, 16))) return NQ_ERR_INVALID_ARG;
+    if (scores_opt && !aligned(scores_opt, 8)) return NQ_ERR_INVALID_ARG;
+    const size_t need = attn_score_ws(p, q_heads, nullptr).bytes;
+    if (!workspace || ws_bytes < need || !aligned(workspace, kAlign)) return NQ_ERR_WORKSPACE;
+    AttnScoreWs w = attn_score_ws(p, q_heads, workspace);
+    nq::AttnScoreArgs a;
+    a.K = (const uint16_t *)K;
+    a.Q = (const uint16_t *)Q_obs;
+    a.bias = w.bias;
+    a.colsum = w.colsum;
+    a.scores = scores_opt ? scores_opt : w.scores;
+    a.H = H;
+    a.G = G;
+    a.W = W;
+    a.T = T;
+    a.R = G * W;
+    a.layer_begin = p->layer_begin;
+    a.row_chunks = (a.R + nq::kAttnRows - 1) / nq::kAttnRows;
+    const int c_end = T - W;
+    a.key_chunks = c_end > 0 ? (c_end + nq::kAttnKeys - 1) / nq::kAttnKeys : 0;
+    const int64_t pairs = (int64_t)Lc * H;
+    hipStream_t s = as_stream(stream);
+    clear_error();
+    if (a.R > 0 && a.key_chunks > 0) {
+        hipLaunchKernelGGL(nq::k_attn_rowbias, dim3((uint32_t)(pairs * a.row_chunks)),
+                           dim3(nq::kAttnThreads), 0, s, a);
+        hipLaunchKernelGGL(nq::k_attn_colsum, dim3((uint32_t)(pairs * a.key_chunks)),
+                           dim3(nq::kAttnThreads), 0, s, a);
+    }
+    if (c_end > 0) {
+        const int64_t n = (int64_t)Lc * c_end;
+        hipLaunchKernelGGL(nq::k_attn_finish, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s,
+                           a, Lc);
+    }
+    hipLaunchKernelGGL(nq::k_select, dim3(Lc), dim3(nq::kSelThreads), 0, s, a.scores, T, W,
+                       n_keep, positions);
+    return launched("nq_score_evict_attn");
 }
 
 static nq::CodecArgs codec_args(const nq_params *p, const int32_t *positions,
