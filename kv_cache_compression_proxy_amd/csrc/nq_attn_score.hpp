@@ -180,6 +180,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_rowbias(AttnScoreArgs a)
             l_run = __builtin_fmaf(l_run, __builtin_amdgcn_exp2f(m_run - mref), sum16(e));
             m_run = mn;
         }
+        asm volatile("" ::"v"(l_run), "v"(m_run) : "memory");   // as in k_attn_colsum
         if (kt + 1 < nkt) store_tile(buf ^ 1);
         __syncthreads();
     };
@@ -206,8 +207,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_rowbias(AttnScoreArgs a)
 // D = Q_tile (32 rows) x K^T (32 keys): every lane accumulates 16 rows of its own key column.
 __global__ __launch_bounds__(kAttnThreads) void k_attn_colsum(AttnScoreArgs a)
 {
-    __shared__ __align__(16) _Float16 qs[2][kQTile][kRowPad];
-    __shared__ __align__(16) float bs[2][kQTile];
+    __shared__ __align__(16) _Float16 qs[3][kQTile][kRowPad];
+    __shared__ __align__(16) float bs[3][kQTile];
     int pair, chunk;
     pair_chunk(blockIdx.x, (int)(gridDim.x / (uint32_t)a.key_chunks), a.key_chunks, pair, chunk);
     const int lc = pair / a.H, h = pair % a.H;
@@ -256,34 +257,58 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_colsum(AttnScoreArgs a)
         if (threadIdx.x < kQTile) bs[buf][threadIdx.x] = sb;
     };
 
-    float col = 0.0f;
-    if (nqt > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    wait_vmem();
-    __syncthreads();
-    for (int qt = 0; qt < nqt; qt++) {
-        const int buf = qt & 1;
-        if (qt + 1 < nqt) load_tile(qt + 1);
+    // Software pipeline over the query tiles, three LDS buffers: in iteration qt the matrix
+    // steps of tile qt + 1 are issued (into the second accumulator) before the exponentials of
+    // tile qt, so the matrix pipe and the vector ALU work at the same time; tile qt + 2 is
+    // fetched meanwhile and stored at the end of the iteration.
+    auto chain = [&](int buf) {
         f32x16 acc = {};
 #pragma unroll
         for (int s = 0; s < 8; s++)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(lds_f16x8(&qs[buf][n][h2 * 64 + s * 8]),
                                                          kb[s], acc, 0, 0, 0);
+        return acc;
+    };
+    float col = 0.0f;
+    if (nqt > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    if (nqt > 1) {
+        load_tile(1);
+        store_tile(1);
+    }
+    wait_vmem();
+    __syncthreads();
+    // one pipeline step: issue tile qt + 1 into `next`, exponentiate tile qt from `cur`
+    // (buffer qt % 3), store tile qt + 2; two steps per loop trip with the accumulators'
+    // roles swapped, so no accumulator is copied
+    auto step = [&](int qt, const f32x16 &cur, f32x16 &next) {
+        const int buf = qt % 3, nbuf = (qt + 1) % 3, fbuf = (qt + 2) % 3;
+        if (qt + 2 < nqt) load_tile(qt + 2);
+        if (qt + 1 < nqt) next = chain(nbuf);
         // row of accumulator i: (i / 4) * 8 + h2 * 4 + i % 4 -> biases in 4 runs of 4
         float e[16];
 #pragma unroll
         for (int i4 = 0; i4 < 4; i4++) {
             const float4 b = *reinterpret_cast<const float4 *>(&bs[buf][i4 * 8 + h2 * 4]);
-            e[4 * i4 + 0] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[4 * i4 + 0], kLog2eInvSqrt128, -b.x));
-            e[4 * i4 + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[4 * i4 + 1], kLog2eInvSqrt128, -b.y));
-            e[4 * i4 + 2] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[4 * i4 + 2], kLog2eInvSqrt128, -b.z));
-            e[4 * i4 + 3] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[4 * i4 + 3], kLog2eInvSqrt128, -b.w));
+            e[4 * i4 + 0] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[4 * i4 + 0], kLog2eInvSqrt128, -b.x));
+            e[4 * i4 + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[4 * i4 + 1], kLog2eInvSqrt128, -b.y));
+            e[4 * i4 + 2] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[4 * i4 + 2], kLog2eInvSqrt128, -b.z));
+            e[4 * i4 + 3] = __builtin_amdgcn_exp2f(__builtin_fmaf(cur[4 * i4 + 3], kLog2eInvSqrt128, -b.w));
         }
         col += sum16(e);
-        if (qt + 1 < nqt) store_tile(buf ^ 1);
+        // keep the store of the prefetched tile (and its wait for the load) below the
+        // exponentials: an empty asm that consumes their sum and orders memory; the compiler
+        // would otherwise hoist the store, stall on the load, and sink the math past the barrier
+        asm volatile("" ::"v"(col) : "memory");
+        if (qt + 2 < nqt) store_tile(fbuf);
         __syncthreads();
+    };
+    f32x16 acc0 = nqt > 0 ? chain(0) : f32x16{}, acc1 = {};
+    for (int qt = 0; qt < nqt; qt += 2) {
+        step(qt, acc0, acc1);
+        if (qt + 1 < nqt) step(qt + 1, acc1, acc0);
     }
     col += __shfl_xor(col, 32);   // lanes n and n + 32 summed different rows of one key
     if (valid && h2 == 0) a.colsum[(size_t)pair * T + t] = col;
