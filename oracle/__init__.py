@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the CP
 of ``bench.py`` use it. The GPU library never imports it and shares no code with it.
 
 Every function here is marshalling only; the arithmetic lives in nq_oracle.c, which cites the
-pages' passages step by step. Arrays are numpy; fp16 data travels as uint16 bit patterns.
+pages' passages step by step. Arrays are numpy; fp16 data travels as uint16 bit patterns. Two
+numpy modules sit beside it: attn_scorer.py (the attention-weight scorer) and lloyd_max.py (the
+equal-bit scalar baseline).
 """
 from __future__ import annotations
 
