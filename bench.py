@@ -56,6 +56,9 @@ def parse():
                     help="time the attention-weight scorer (nq_score_evict_attn, 32 query heads, "
                          "W-query observation window) against the key-key proxy scorer on the "
                          "headline workload instead")
+    ap.add_argument("--scalar", action="store_true",
+                    help="time and compare the equal-bit Lloyd-Max scalar baseline against the E8 "
+                         "codec on the same keep-set instead (throughput, SNR, cosine)")
     ap.add_argument("--entropy", action="store_true",
                     help="compress the workload on the GPU, then measure the host zstd stage's "
                          "post-entropy ratio (off the timed path) instead")
@@ -309,6 +312,105 @@ def attn_score(args):
     print(json.dumps(res), flush=True)
 
 
+def scalar_baseline(args):
+    """E8 codec vs the equal-bit Lloyd-Max scalar baseline on the same keep-set: encode and
+    decode (fp16 out) times, and reconstruction quality (SNR, mean cosine against the original
+    kept rows, fp32 reconstructions) on two sampled layers."""
+    import torch
+    import kv_cache_compression_proxy_amd as nq
+    import kvsynth
+    w = kvsynth.workload(args.workload)
+    p = nq.make_params(w.layers, w.kv_heads, w.tokens, w.window, w.evict_permille, w.bits_k,
+                       w.bits_v, w.rope_base, w.layer_begin, w.layer_end)
+    Lc, H, T = w.compressed_layers, w.kv_heads, w.tokens
+    n = nq.nq_keep_count(p)
+    dev = torch.device("cuda:0")
+    K, V = upload_workload(w, dev)
+    cos, sin = nq.rope_table(p, dev)
+    pos = torch.empty((Lc, n), dtype=torch.int32, device=dev)
+    nq.nq_score_evict(p, K, pos, nq.workspace(nq.nq_score_evict_workspace_bytes(p), dev))
+    ck = torch.empty((Lc, H, n, 128), dtype=torch.int8, device=dev)
+    cv = torch.empty_like(ck)
+    ik = torch.empty((Lc, H, n, 128), dtype=torch.uint8, device=dev)
+    iv = torch.empty_like(ik)
+    sk = torch.empty((Lc, H, n, 16), dtype=torch.float16, device=dev)
+    sv, sk2, sv2 = torch.empty_like(sk), torch.empty_like(sk), torch.empty_like(sk)
+    Ko = torch.empty((Lc, H, n, 128), dtype=torch.float16, device=dev)
+    Vo = torch.empty_like(Ko)
+    ws_d = nq.workspace(nq.nq_decode_workspace_bytes(p), dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    t_e8_enc = timed(lambda: nq.nq_encode(p, K, V, pos, cos, sin, ck, cv, sk, sv, stream))
+    t_e8_dec = timed(lambda: nq.nq_decode(p, ck, cv, sk, sv, pos, cos, sin, Ko, Vo,
+                                          nq.NQ_OUT_F16, ws_d, stream))
+    t_sc_enc = timed(lambda: nq.nq_encode_scalar(p, K, V, pos, cos, sin, ik, iv, sk2, sv2,
+                                                 stream))
+    t_sc_dec = timed(lambda: nq.nq_decode_scalar(p, ik, iv, sk2, sv2, pos, cos, sin, Ko, Vo,
+                                                 nq.NQ_OUT_F16, stream))
+    # quality on two sampled layers, fp32 reconstructions of every kept row
+    q = {"E8": [0.0, 0.0, 0.0, 0.0, 0.0, 0.0], "LloydMax": [0.0, 0.0, 0.0, 0.0, 0.0, 0.0]}
+    cosines = {"E8": [[], []], "LloydMax": [[], []]}
+    for lc in (0, Lc - 1):
+        pl = nq.make_params(1, H, T, w.window, w.evict_permille, w.bits_k, w.bits_v, w.rope_base)
+        layer = w.layer_begin + lc
+        Kl, Vl, Pl = K[layer:layer + 1], V[layer:layer + 1], pos[lc:lc + 1]
+        orig = [Kl[0][:, Pl[0].long()].float(), Vl[0][:, Pl[0].long()].float()]
+        Kf = torch.empty((1, H, n, 128), dtype=torch.float32, device=dev)
+        Vf = torch.empty_like(Kf)
+        nq.nq_decode(pl, ck[lc:lc + 1], cv[lc:lc + 1], sk[lc:lc + 1], sv[lc:lc + 1], Pl, cos,
+                     sin, Kf, Vf, nq.NQ_OUT_F32, nq.workspace(nq.nq_decode_workspace_bytes(pl),
+                                                              dev))
+        Ks, Vs = torch.empty_like(Kf), torch.empty_like(Vf)
+        nq.nq_decode_scalar(pl, ik[lc:lc + 1], iv[lc:lc + 1], sk2[lc:lc + 1], sv2[lc:lc + 1], Pl,
+                            cos, sin, Ks, Vs, nq.NQ_OUT_F32)
+        for name, rec in (("E8", [Kf[0], Vf[0]]), ("LloydMax", [Ks[0], Vs[0]])):
+            for t_ in range(2):
+                x, y = orig[t_].double(), rec[t_].double()
+                q[name][2 * t_] += float((x * x).sum())
+                q[name][2 * t_ + 1] += float(((x - y) ** 2).sum())
+                cosines[name][t_].append(float(torch.nn.functional.cosine_similarity(
+                    x, y, dim=-1).mean()))
+    quality = {}
+    for name in q:
+        quality[name] = {
+            "snr_db_k": round(10 * np.log10(q[name][0] / q[name][1]), 3),
+            "snr_db_v": round(10 * np.log10(q[name][2] / q[name][3]), 3),
+            "cos_k": round(float(np.mean(cosines[name][0])), 5),
+            "cos_v": round(float(np.mean(cosines[name][1])), 5)}
+    kv = Lc * H * n * 2 * 256
+    log(f"[scalar] E8 encode {t_e8_enc:.3f} decode {t_e8_dec:.3f} ms; Lloyd-Max encode "
+        f"{t_sc_enc:.3f} decode {t_sc_dec:.3f} ms; quality {quality}")
+    res = {
+        "metric": "equal-bit comparison: E8 codec vs Lloyd-Max scalar codec (same keep-set, "
+                  "front end and fp16 group scales)",
+        "value": round(quality["E8"]["snr_db_k"] - quality["LloydMax"]["snr_db_k"], 3),
+        "unit": "dB (key SNR, E8 minus Lloyd-Max)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+        "vs_baseline": None, "data": "synthetic",
+        "config": {"workload": w.name, "bits_k": w.bits_k, "bits_v": w.bits_v, "n_keep": n},
+        "ms": {"e8_encode": round(t_e8_enc, 4), "e8_decode": round(t_e8_dec, 4),
+               "lloydmax_encode": round(t_sc_enc, 4), "lloydmax_decode": round(t_sc_dec, 4)},
+        "fp16_kv_GBps": {"e8_encode": round(kv / (t_e8_enc * 1e-3) / 1e9, 1),
+                         "e8_decode": round(kv / (t_e8_dec * 1e-3) / 1e9, 1),
+                         "lloydmax_encode": round(kv / (t_sc_enc * 1e-3) / 1e9, 1),
+                         "lloydmax_decode": round(kv / (t_sc_dec * 1e-3) / 1e9, 1)},
+        "quality_two_sampled_layers": quality,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def entropy_stage(args):
     """Measured post-entropy ratio of a full workload: the GPU compresses it (score, evict,
     encode), then the host zstd stage sizes the delta streams, scales and keep-set bitmaps of
@@ -495,6 +597,9 @@ def main():
         return
     if args.entropy:
         entropy_stage(args)
+        return
+    if args.scalar:
+        scalar_baseline(args)
         return
     import torch
     import kv_cache_compression_proxy_amd as nq

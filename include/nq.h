@@ -193,6 +193,34 @@ nq_status nq_decode_attend(const nq_params *p, const int8_t *codes_k, const int8
                            int32_t q_heads, float *out, void *workspace, size_t ws_bytes,
                            void *stream);
 
+/* Equal-bit scalar baseline (page "Lloyd-Max量化": Lloyd-Max quantization by alternating
+ * nearest-level assignment and centroid updates, then table lookup; "3-bit量化的设计选择"). The
+ * Lloyd-Max table of the unit Gaussian with 2^bits levels (1 <= bits <= 4), computed on the
+ * host once per bit width and made exactly antisymmetric: levels [2^bits] ascending,
+ * thresholds [2^bits - 1] (midpoints). Host memory, owned by the caller. */
+nq_status nq_lloyd_max_table(int32_t bits, double *levels, double *thresholds);
+
+/* The codec's front end (keys rotated back by their position, normalised Hadamard rotation)
+ * with a per-coordinate Lloyd-Max quantizer in place of the E8 step, at bits_k / bits_v bits:
+ * per 8-float group the fp16 scale s = RMS of the group (fp32, squares added in dim order,
+ * rounded to nearest fp16) and per coordinate the index of u = x / s in the table (number of
+ * thresholds strictly below u; an all-zero group gets 2^(b-1)). No delta coding.
+ *   idx_k, idx_v        uint8 [L_c][H][n_keep][128] out (8-byte aligned)
+ *   scales_k, scales_v  fp16 [L_c][H][n_keep][16] out
+ *   other arguments as for nq_encode */
+nq_status nq_encode_scalar(const nq_params *p, const void *K, const void *V,
+                           const int32_t *positions, const float *rope_cos, const float *rope_sin,
+                           uint8_t *idx_k, uint8_t *idx_v, void *scales_k, void *scales_v,
+                           void *stream);
+
+/* Inverse of nq_encode_scalar: x = s * level[index], inverse normalised Hadamard transform,
+ * keys rotated forward by their position; fp16 or fp32 output as for nq_decode (no workspace:
+ * the indices carry no running sum). */
+nq_status nq_decode_scalar(const nq_params *p, const uint8_t *idx_k, const uint8_t *idx_v,
+                           const void *scales_k, const void *scales_v, const int32_t *positions,
+                           const float *rope_cos, const float *rope_sin, void *K_out,
+                           void *V_out, nq_out_dtype out_dtype, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *nq_status_string(nq_status s);
 

@@ -1,7 +1,7 @@
 """Python binding of libnq, the MI355X (gfx950) KV-cache compression hot path.
 
 Argument marshalling only: every step runs in the HIP kernels of ``libnq.so`` (built in-tree by
-``python -m kv_cache_compression_proxy_amd.build``). PyTorch supplies device memory and streams.
+``python kv_cache_compression_proxy_amd/build.py``). PyTorch supplies device memory and streams.
 Importing this package without the built library raises ImportError -- there is no fallback.
 
 Low-level functions carry the C names of ``include/nq.h`` (``nq_score_evict``, ``nq_encode``,
@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libnq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      f"`python -m kv_cache_compression_proxy_amd.build` (no CPU fallback exists)")
+                      f"`python kv_cache_compression_proxy_amd/build.py` (no CPU fallback exists)")
 
 # torch ships its own HIP runtime; importing it first makes libnq's libamdhip64.so.7 dependency
 # resolve (by soname) to that same, already loaded runtime, so both share one device context.
@@ -35,7 +35,8 @@ EXPORTED = ("nq_keep_count", "nq_check_params", "nq_score_evict_workspace_bytes"
             "nq_decode_workspace_bytes", "nq_attend_workspace_bytes", "nq_rope_table",
             "nq_score_evict", "nq_encode", "nq_decode", "nq_attend_decode",
             "nq_decode_attend_workspace_bytes", "nq_decode_attend",
-            "nq_score_evict_attn_workspace_bytes", "nq_score_evict_attn", "nq_status_string")
+            "nq_score_evict_attn_workspace_bytes", "nq_score_evict_attn", "nq_lloyd_max_table",
+            "nq_encode_scalar", "nq_decode_scalar", "nq_status_string")
 
 
 class NqParams(C.Structure):
@@ -67,6 +68,9 @@ _sig = {
                                    C.c_size_t, _v]),
     "nq_score_evict_attn_workspace_bytes": (C.c_size_t, [_P, C.c_int32]),
     "nq_score_evict_attn": (C.c_int, [_P, _v, _v, C.c_int32, _v, _v, _v, C.c_size_t, _v]),
+    "nq_lloyd_max_table": (C.c_int, [C.c_int32, _v, _v]),
+    "nq_encode_scalar": (C.c_int, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v]),
+    "nq_decode_scalar": (C.c_int, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, C.c_int, _v]),
     "nq_status_string": (C.c_char_p, [C.c_int]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -185,6 +189,29 @@ def nq_decode_attend(p, codes_k, codes_v, scales_k, scales_v, positions, rope_co
         C.byref(p), _ptr(codes_k), _ptr(codes_v), _ptr(scales_k), _ptr(scales_v), _ptr(positions),
         _ptr(rope_cos), _ptr(rope_sin), _ptr(Q), q_heads, _ptr(out), _ptr(workspace), ws,
         _stream(stream)))
+
+
+def nq_lloyd_max_table(bits: int):
+    """-> (levels, thresholds) float64 numpy arrays of the library's Lloyd-Max table."""
+    import numpy as np
+    y = np.zeros(1 << bits, np.float64)
+    t = np.zeros(max((1 << bits) - 1, 1), np.float64)
+    _ok("nq_lloyd_max_table", _lib.nq_lloyd_max_table(bits, y.ctypes.data, t.ctypes.data))
+    return y, t[:(1 << bits) - 1]
+
+
+def nq_encode_scalar(p, K, V, positions, rope_cos, rope_sin, idx_k, idx_v, scales_k, scales_v,
+                     stream=None):
+    _ok("nq_encode_scalar", _lib.nq_encode_scalar(
+        C.byref(p), _ptr(K), _ptr(V), _ptr(positions), _ptr(rope_cos), _ptr(rope_sin),
+        _ptr(idx_k), _ptr(idx_v), _ptr(scales_k), _ptr(scales_v), _stream(stream)))
+
+
+def nq_decode_scalar(p, idx_k, idx_v, scales_k, scales_v, positions, rope_cos, rope_sin, K_out,
+                     V_out, out_dtype, stream=None):
+    _ok("nq_decode_scalar", _lib.nq_decode_scalar(
+        C.byref(p), _ptr(idx_k), _ptr(idx_v), _ptr(scales_k), _ptr(scales_v), _ptr(positions),
+        _ptr(rope_cos), _ptr(rope_sin), _ptr(K_out), _ptr(V_out), out_dtype, _stream(stream)))
 
 
 def nq_status_string(status: int) -> str:

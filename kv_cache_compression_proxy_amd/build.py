@@ -1,6 +1,8 @@
 """Builds libnq.so (the HIP library for gfx950) in-tree with hipcc.
 
-Run ``python -m kv_cache_compression_proxy_amd.build`` (or ``__graft_entry__.build()``).
+Run ``python kv_cache_compression_proxy_amd/build.py`` (or ``__graft_entry__.build()``). It is
+a plain script, run by path: importing the package loads the library, which must not be needed
+to build it (a fresh checkout has none, an old build may lack newer entry points).
 """
 from __future__ import annotations
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -13,6 +14,7 @@
 #include "nq_attn_score.hpp"
 #include "nq_codec.hpp"
 #include "nq_fused.hpp"
+#include "nq_scalar.hpp"
 #include "nq_score.hpp"
 
 namespace {
@@ -190,6 +192,79 @@ AttnScoreWs attn_score_ws(const nq_params *p, int32_t q_heads, void *base)
     w.scores = (double *)((char *)base + b + c);
     w.bytes = b + c + d;
     return w;
+}
+
+// Lloyd-Max quantizer of N(0, 1) with 2^bits levels: from levels evenly spaced on [-2, 2],
+// alternate thresholds = midpoints of neighbouring levels and levels = the mean of N(0, 1) over
+// each cell, until no level moves by 1e-15; then make the table exactly antisymmetric (N(0, 1)
+// is symmetric; the middle threshold becomes exactly 0).
+double gauss_pdf(double x) { return isfinite(x) ? exp(-0.5 * x * x) / sqrt(2.0 * M_PI) : 0.0; }
+double gauss_cdf(double x)
+{
+    if (x == INFINITY) return 1.0;
+    if (x == -INFINITY) return 0.0;
+    return 0.5 * erfc(-x / sqrt(2.0));
+}
+
+void lloyd_max(int bits, double *y, double *t)
+{
+    const int n = 1 << bits;
+    for (int i = 0; i < n; i++) y[i] = n > 1 ? i * (4.0 / (n - 1)) + -2.0 : 0.0;
+    if (n > 1) y[n - 1] = 2.0;
+    double e[17], yn[16];
+    for (int it = 0; it < 200000; it++) {
+        e[0] = -INFINITY;
+        e[n] = INFINITY;
+        for (int i = 0; i + 1 < n; i++) e[i + 1] = 0.5 * (y[i] + y[i + 1]);
+        double d = 0.0;
+        for (int i = 0; i < n; i++) {
+            yn[i] = (gauss_pdf(e[i]) - gauss_pdf(e[i + 1])) / (gauss_cdf(e[i + 1]) - gauss_cdf(e[i]));
+            d = fmax(d, fabs(yn[i] - y[i]));
+        }
+        for (int i = 0; i < n; i++) y[i] = yn[i];
+        if (d < 1e-15) break;
+    }
+    double ys[16];
+    for (int i = 0; i < n; i++) ys[i] = 0.5 * (y[i] - y[n - 1 - i]);
+    for (int i = 0; i < n; i++) y[i] = ys[i];
+    for (int i = 0; i + 1 < n; i++) t[i] = 0.5 * (y[i] + y[i + 1]);
+}
+
+struct LloydTables {
+    double y[5][16], t[5][15];
+    std::once_flag once;
+};
+LloydTables &lloyd_tables()
+{
+    static LloydTables tb;
+    std::call_once(tb.once, [] {
+        for (int b = 1; b <= 4; b++) lloyd_max(b, tb.y[b], tb.t[b]);
+    });
+    return tb;
+}
+
+nq::ScalarArgs scalar_args(const nq_params *p, const int32_t *positions, const float *rope_cos,
+                           const float *rope_sin)
+{
+    nq::ScalarArgs a;
+    memset(&a, 0, sizeof(a));
+    a.positions = positions;
+    a.rope_cos = rope_cos;
+    a.rope_sin = rope_sin;
+    a.H = p->kv_heads;
+    a.T = p->tokens;
+    a.layer_begin = p->layer_begin;
+    a.n_keep = keep_count(p);
+    a.tiles = (a.n_keep + nq::kScalarTile - 1) / nq::kScalarTile;
+    LloydTables &tb = lloyd_tables();
+    const int bits[2] = {p->bits_k, p->bits_v};
+    for (int tn = 0; tn < 2; tn++) {
+        const int b = bits[tn], n = 1 << b;
+        a.bits[tn] = b;
+        for (int i = 0; i < 15; i++) a.thr[tn][i] = i + 1 < n ? (float)tb.t[b][i] : INFINITY;
+        for (int i = 0; i < 16; i++) a.lev[tn][i] = i < n ? (float)tb.y[b][i] : 0.0f;
+    }
+    return a;
 }
 
 }  // namespace
@@ -504,6 +579,77 @@ nq_status nq_decode_attend(const nq_params *p, const int8_t *codes_k, const int8
         break;
     }
     return launched("nq_decode_attend");
+}
+
+nq_status nq_lloyd_max_table(int32_t bits, double *levels, double *thresholds)
+{
+    if (bits < 1 || bits > 4 || !levels || !thresholds) return NQ_ERR_INVALID_ARG;
+    LloydTables &tb = lloyd_tables();
+    for (int i = 0; i < (1 << bits); i++) levels[i] = tb.y[bits][i];
+    for (int i = 0; i + 1 < (1 << bits); i++) thresholds[i] = tb.t[bits][i];
+    return NQ_OK;
+}
+
+nq_status nq_encode_scalar(const nq_params *p, const void *K, const void *V,
+                           const int32_t *positions, const float *rope_cos, const float *rope_sin,
+                           uint8_t *idx_k, uint8_t *idx_v, void *scales_k, void *scales_v,
+                           void *stream)
+{
+    nq_status st = check(p);
+    if (st != NQ_OK) return st;
+    const int32_t Lc = compressed_layers(p);
+    if (Lc == 0 || p->tokens == 0) return NQ_OK;
+    const void *ptrs16[] = {K, V, rope_cos, rope_sin};
+    for (const void *q : ptrs16)
+        if (!q || !aligned(q, 16)) return NQ_ERR_INVALID_ARG;
+    if (!idx_k || !idx_v || !aligned(idx_k, 8) || !aligned(idx_v, 8) || !positions ||
+        !aligned(positions, 4) || !scales_k || !scales_v || !aligned(scales_k, 2) ||
+        !aligned(scales_v, 2))
+        return NQ_ERR_INVALID_ARG;
+    nq::ScalarArgs a = scalar_args(p, positions, rope_cos, rope_sin);
+    a.K = (const uint16_t *)K;
+    a.V = (const uint16_t *)V;
+    a.idx_k = idx_k;
+    a.idx_v = idx_v;
+    a.scales_k = (uint16_t *)scales_k;
+    a.scales_v = (uint16_t *)scales_v;
+    const int64_t blocks = (int64_t)Lc * 2 * p->kv_heads * a.tiles;
+    clear_error();
+    hipLaunchKernelGGL(nq::k_encode_scalar, dim3((uint32_t)blocks), dim3(nq::kCodecThreads), 0,
+                       as_stream(stream), a);
+    return launched("nq_encode_scalar");
+}
+
+nq_status nq_decode_scalar(const nq_params *p, const uint8_t *idx_k, const uint8_t *idx_v,
+                           const void *scales_k, const void *scales_v, const int32_t *positions,
+                           const float *rope_cos, const float *rope_sin, void *K_out,
+                           void *V_out, nq_out_dtype out_dtype, void *stream)
+{
+    nq_status st = check(p);
+    if (st != NQ_OK) return st;
+    if (out_dtype != NQ_OUT_F16 && out_dtype != NQ_OUT_F32) return NQ_ERR_INVALID_ARG;
+    const int32_t Lc = compressed_layers(p);
+    if (Lc == 0 || p->tokens == 0) return NQ_OK;
+    const void *ptrs16[] = {rope_cos, rope_sin, K_out, V_out};
+    for (const void *q : ptrs16)
+        if (!q || !aligned(q, 16)) return NQ_ERR_INVALID_ARG;
+    if (!idx_k || !idx_v || !aligned(idx_k, 8) || !aligned(idx_v, 8) || !positions ||
+        !aligned(positions, 4) || !scales_k || !scales_v || !aligned(scales_k, 2) ||
+        !aligned(scales_v, 2))
+        return NQ_ERR_INVALID_ARG;
+    nq::ScalarArgs a = scalar_args(p, positions, rope_cos, rope_sin);
+    a.idx_k = (uint8_t *)idx_k;
+    a.idx_v = (uint8_t *)idx_v;
+    a.scales_k = (uint16_t *)scales_k;
+    a.scales_v = (uint16_t *)scales_v;
+    a.out_k = K_out;
+    a.out_v = V_out;
+    a.out_f32 = out_dtype == NQ_OUT_F32;
+    const int64_t blocks = (int64_t)Lc * 2 * p->kv_heads * a.tiles;
+    clear_error();
+    hipLaunchKernelGGL(nq::k_decode_scalar, dim3((uint32_t)blocks), dim3(nq::kCodecThreads), 0,
+                       as_stream(stream), a);
+    return launched("nq_decode_scalar");
 }
 
 nq_status nq_attend_decode(const nq_params *p, const void *Q, int32_t q_heads, const void *K,

@@ -201,19 +201,21 @@ __device__ __forceinline__ void e8_nearest_code(const float u[8], uint32_t &w0, 
 
 // Encodes one kept token of one chain for this lane's 8 dims. Returns the absolute code bytes
 // (offset +64) and the fp16 scale bits of this lane's group.
+// The codec front end for one kept token (row at position p; X points at this lane's 8 dims
+// of the chain's first row): the fp16 row, for keys the rotary embedding removed at p, then
+// the Hadamard butterflies. x = group_sign(g) times the unnormalised rotated row.
 template <bool IS_KEY>
-__device__ __forceinline__ uint2 encode_token(const CodecArgs &a, const uint16_t *__restrict__ X,
-                                              int p, int g, float rho, float rho_inv,
-                                              uint32_t &s16)
+__device__ __forceinline__ void front_end(const float *__restrict__ rope_cos,
+                                          const float *__restrict__ rope_sin,
+                                          const uint16_t *__restrict__ X, int p, int g, float x[8])
 {
-    float x[8];
     load_f16x8_stream(X + (uint32_t)p * kHeadDim, x);   // each K/V row is read once
     if (IS_KEY) {
         // RoPE removal, split-half pairs (i, i + 64) = lanes (g, g ^ 8):
         // x_i = a*C + b*S, x_{i+64} = b*C - a*S with (a, b) = (k_i, k_{i+64}).
         float c[8], s[8];
-        load_f32x8(a.rope_cos + (size_t)p * 64 + 8 * (g & 7), c);
-        load_f32x8(a.rope_sin + (size_t)p * 64 + 8 * (g & 7), s);
+        load_f32x8(rope_cos + (size_t)p * 64 + 8 * (g & 7), c);
+        load_f32x8(rope_sin + (size_t)p * 64 + 8 * (g & 7), s);
         const float sg = g >= 8 ? -1.0f : 1.0f;
 #pragma unroll
         for (int k = 0; k < 8; k++) {
@@ -223,6 +225,15 @@ __device__ __forceinline__ uint2 encode_token(const CodecArgs &a, const uint16_t
         }
     }
     hadamard_butterflies(x, g);
+}
+
+template <bool IS_KEY>
+__device__ __forceinline__ uint2 encode_token(const CodecArgs &a, const uint16_t *__restrict__ X,
+                                              int p, int g, float rho, float rho_inv,
+                                              uint32_t &s16)
+{
+    float x[8];
+    front_end<IS_KEY>(a.rope_cos, a.rope_sin, X, p, g, x);
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; k++) amax = fmaxf(amax, __builtin_fabsf(x[k]));
@@ -459,6 +470,16 @@ __device__ __forceinline__ uint2 chain_lookback(uint32_t *lb_agg, uint32_t *lb_i
     return excl;
 }
 
+// RoPE at a stored position on x = group_sign(g) times a rotated-back key row:
+// k_i = x_i*C - x_{i+64}*S, k_{i+64} = x_{i+64}*C + x_i*S. The partner lane (group g ^ 8)
+// carries the opposite lane sign, hence the flipped +-.
+__device__ __forceinline__ void rope_redo(float x[8], int g, const float cr[8], const float sr[8])
+{
+    const float sg = g >= 8 ? -1.0f : 1.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++) x[k] = __builtin_fmaf(sg, lane_xor8(x[k]) * sr[k], x[k] * cr[k]);
+}
+
 // Reconstructs one token of one chain for this lane's 8 dims: x = group_sign(g) times the
 // reconstructed row (dims 8g..8g+7). code: the token's absolute code bytes as c + 64, s16:
 // this group's scale, (cr, sr): the rotary table row of the token's position (keys only).
@@ -514,28 +535,18 @@ __device__ __forceinline__ void decode_row(int g, uint2 code, uint32_t s16, cons
           "=&v"(x[6]), "=&v"(x[7])
         : "v"(q0), "v"(q1), "v"(q2), "v"(q3), "v"(hs));
     hadamard_cross_lane(x, g);   // x = group_sign(g) * (the reconstructed row)
-    if (IS_KEY) {
-        // RoPE at the stored position: k_i = x_i*C - x_{i+64}*S, k_{i+64} = x_{i+64}*C + x_i*S.
-        // The partner lane g^8 carries the opposite lane sign, hence the flipped +-.
-        const float sg = g >= 8 ? -1.0f : 1.0f;
-#pragma unroll
-        for (int k = 0; k < 8; k++)
-            x[k] = __builtin_fmaf(sg, lane_xor8(x[k]) * sr[k], x[k] * cr[k]);
-    }
+    if (IS_KEY) rope_redo(x, g, cr, sr);
 }
 
-// decode_row, then the row stored (fp32 or fp16) at row j of the chain starting at row_off
-template <bool IS_KEY>
-__device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off, int j, int g,
-                                             uint2 code, uint32_t s16, const float cr[8],
-                                             const float sr[8])
+// Stores this lane's 8 dims of a reconstructed row (x = group_sign(g) times the row) as fp32
+// or fp16 at row j of the chain starting at row_off.
+__device__ __forceinline__ void store_row(void *out, bool out_f32, size_t row_off, int j, int g,
+                                          float x[8])
 {
-    float x[8];
-    decode_row<IS_KEY>(g, code, s16, cr, sr, x);
     const uint32_t sbit = (__popc(g & 15) & 1) ? 0x80000000u : 0u;   // group_sign as a sign bit
     const size_t o = row_off + (size_t)j * kHeadDim + 8 * g;
-    if (a.out_f32) {
-        float *dst = (float *)(IS_KEY ? a.out_k : a.out_v) + o;
+    if (out_f32) {
+        float *dst = (float *)out + o;
 #pragma unroll
         for (int k = 0; k < 8; k++) x[k] = __uint_as_float(__float_as_uint(x[k]) ^ sbit);
         const u32x4 v0 = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
@@ -547,7 +558,7 @@ __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off,
         __builtin_nontemporal_store(v1, reinterpret_cast<u32x4 *>(dst + 4));
     } else {
         // rounding to fp16 commutes with the sign, which is flipped on the packed halves
-        uint16_t *dst = (uint16_t *)(IS_KEY ? a.out_k : a.out_v) + o;
+        uint16_t *dst = (uint16_t *)out + o;
         const uint32_t s2 = sbit | (sbit >> 16);
         u32x4 v;
         v.x = f2h_pack(x[0], x[1]) ^ s2;
@@ -556,6 +567,17 @@ __device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off,
         v.w = f2h_pack(x[6], x[7]) ^ s2;
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
     }
+}
+
+// decode_row, then the row stored at row j of the chain starting at row_off
+template <bool IS_KEY>
+__device__ __forceinline__ void decode_store(const CodecArgs &a, size_t row_off, int j, int g,
+                                             uint2 code, uint32_t s16, const float cr[8],
+                                             const float sr[8])
+{
+    float x[8];
+    decode_row<IS_KEY>(g, code, s16, cr, sr, x);
+    store_row(IS_KEY ? a.out_k : a.out_v, a.out_f32, row_off, j, g, x);
 }
 
 struct DecodeShared {

@@ -18,6 +18,7 @@ index 2^(b-1) everywhere (its reconstruction is 0 whatever the index).
 """
 from __future__ import annotations
 
+import functools
 import math
 
 import numpy as np
@@ -53,6 +54,9 @@ def lloyd_max_gaussian(bits: int, tol: float = 1e-15, max_iter: int = 200000):
             y = y_new
             break
         y = y_new
+    # N(0, 1) is symmetric: make the table exactly antisymmetric, so that the middle
+    # threshold is exactly 0 (rounding noise of order 1e-17 would otherwise decide the side of 0)
+    y = 0.5 * (y - y[::-1])
     return y, 0.5 * (y[:-1] + y[1:])
 
 
@@ -71,9 +75,16 @@ def gaussian_mse(levels: np.ndarray, thresholds: np.ndarray) -> float:
     return d
 
 
-def tables_f32(bits: int):
+@functools.lru_cache(maxsize=None)
+def _tables_f32_cached(bits: int):
     y, t = lloyd_max_gaussian(bits)
     return y.astype(np.float32), t.astype(np.float32)
+
+
+def tables_f32(bits: int):
+    """The fp32 tables the quantizer compares and reconstructs with (copies of a cached pair)."""
+    y, t = _tables_f32_cached(bits)
+    return y.copy(), t.copy()
 
 
 def quantize_group(x8: np.ndarray, bits: int):

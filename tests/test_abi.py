@@ -5,6 +5,7 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 
 import kv_cache_compression_proxy_amd as nq
@@ -137,3 +138,16 @@ def test_presets():
                                                                 w.bits_k, w.bits_v)
     with pytest.raises(ValueError):
         nq.params_for("asym", 1, 1, 1)
+
+
+def test_lloyd_max_tables_match_the_oracle():
+    from oracle.lloyd_max import lloyd_max_gaussian
+    for bits in (1, 2, 3, 4):
+        y, t = nq.nq_lloyd_max_table(bits)
+        yo, to = lloyd_max_gaussian(bits)
+        assert np.max(np.abs(y - yo)) < 1e-12 and np.max(np.abs(t - to)) < 1e-12
+        # the kernels compare in fp32: both sides must round to the same fp32 values
+        assert np.array_equal(y.astype(np.float32), yo.astype(np.float32))
+        assert np.array_equal(t.astype(np.float32), to.astype(np.float32))
+    with pytest.raises(nq.NqError):
+        nq.nq_lloyd_max_table(5)

@@ -1,0 +1,84 @@
+"""GPU parity of the equal-bit scalar baseline (nq_encode_scalar / nq_decode_scalar) against its
+oracle (oracle/lloyd_max.py), on the oracle's keep-set of seeded inputs.
+
+Bars: indices and fp16 scales bit-exact, except in groups the oracle flags as near-ties (a
+coordinate within 1e-6 of a threshold, or the RMS within 1e-6 of an fp16 rounding step),
+which are counted; reconstructions (fp32 output) within 1e-5 x the token-head's largest group
+scale of the oracle's fp64 decode of the same indices; the GPU decode of the oracle's own
+indices likewise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_compression_proxy_amd as nq
+import kvsynth
+import oracle
+from oracle import lloyd_max as lm
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+RECON_TOL = 1e-5
+
+
+def run(T, W, e, bits_k, bits_v, layer=0):
+    w = kvsynth.workload(0).with_(tokens=T, window=W, evict_permille=e, bits_k=bits_k,
+                                  bits_v=bits_v)
+    H = w.kv_heads
+    K_l, V_l = kvsynth.layer_kv(w, layer)
+    Ct, St = oracle.rope_table(T, w.rope_base)
+    pos, _, _ = oracle.select_layer(oracle.layer_scores(K_l, W), W, e)
+    ora = lm.encode_layer(K_l, V_l, pos, Ct, St, bits_k, bits_v)
+    p = nq.make_params(1, H, T, W, e, bits_k, bits_v, w.rope_base)
+    n = nq.nq_keep_count(p)
+    assert n == pos.size
+    dev = "cuda"
+    K = torch.from_numpy(K_l[None]).to(dev)
+    V = torch.from_numpy(V_l[None]).to(dev)
+    P = torch.from_numpy(pos[None].astype(np.int32)).to(dev)
+    cos, sin = nq.rope_table(p, dev)
+    ik = torch.empty((1, H, n, 128), dtype=torch.uint8, device=dev)
+    iv = torch.empty_like(ik)
+    sk = torch.empty((1, H, n, 16), dtype=torch.float16, device=dev)
+    sv = torch.empty_like(sk)
+    nq.nq_encode_scalar(p, K, V, P, cos, sin, ik, iv, sk, sv)
+    Ko = torch.empty((1, H, n, 128), dtype=torch.float32, device=dev)
+    Vo = torch.empty_like(Ko)
+    nq.nq_decode_scalar(p, ik, iv, sk, sv, P, cos, sin, Ko, Vo, nq.NQ_OUT_F32)
+    # the oracle's indices through the GPU decode
+    Ko2, Vo2 = torch.empty_like(Ko), torch.empty_like(Vo)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a[None])).to(dev)
+    nq.nq_decode_scalar(p, t(ora["idx_k"]), t(ora["idx_v"]), t(ora["scales_k"].view(np.float16)),
+                        t(ora["scales_v"].view(np.float16)), P, cos, sin, Ko2, Vo2,
+                        nq.NQ_OUT_F32)
+    torch.cuda.synchronize()
+    st = {}
+    for name, idx_g, sc_g, bits in (("k", ik, sk, bits_k), ("v", iv, sv, bits_v)):
+        gi = idx_g[0].cpu().numpy()
+        gs = sc_g[0].cpu().numpy().view(np.uint16)
+        oi, os_, near = ora["idx_" + name], ora["scales_" + name], ora["near_" + name]
+        bad = (gi.reshape(H, n, 16, 8) != oi.reshape(H, n, 16, 8)).any(-1) | (gs != os_)
+        st["mismatch_" + name] = int(bad.sum())
+        st["near_" + name] = int(near.sum())
+        assert not np.any(bad & ~near), f"{name}: mismatches outside flagged near-ties"
+        assert gi.max() < (1 << bits)
+    Kh, Vh = lm.decode_layer(ora["idx_k"], ora["idx_v"], ora["scales_k"], ora["scales_v"], pos,
+                             Ct, St, bits_k, bits_v)
+    for name, hat_ora, got, got2, sc in (("k", Kh, Ko, Ko2, ora["scales_k"]),
+                                         ("v", Vh, Vo, Vo2, ora["scales_v"])):
+        smax = np.vectorize(oracle.h2f)(sc.astype(np.int64)).max(axis=-1)[..., None]
+        ok_rows = ~(ora["near_" + name].any(-1))[..., None]
+        e1 = np.abs(got[0].cpu().numpy() - hat_ora) / np.maximum(smax, 1e-30)
+        e2 = np.abs(got2[0].cpu().numpy() - hat_ora) / np.maximum(smax, 1e-30)
+        st["recon_" + name] = float((e1 * ok_rows).max())
+        st["recon_oracle_idx_" + name] = float(e2.max())
+        assert st["recon_" + name] <= RECON_TOL and st["recon_oracle_idx_" + name] <= RECON_TOL
+    return st
+
+
+@pytest.mark.parametrize("T,W,e,bk,bv", [(2048, 128, 600, 3, 2), (700, 50, 400, 4, 2),
+                                         (300, 16, 700, 2, 3), (129, 16, 0, 3, 3)])
+def test_scalar_parity(T, W, e, bk, bv):
+    st = run(T, W, e, bk, bv)
+    say(f"[scalar] T={T} W={W} e={e} K{bk}V{bv}: {st}")
