@@ -105,7 +105,7 @@ DecodeWs decode_ws(const nq_params *p, void *base)
     DecodeWs w;
     w.tiles = compressed_layers(p) * 2 * p->kv_heads * decode_tiles(p);
     const size_t words = (size_t)w.tiles * 16 * 4;
-    const size_t t = align_up(2 * sizeof(uint32_t));
+    const size_t t = align_up(nq::kTicketWords * sizeof(uint32_t));
     const size_t v = align_up(words * sizeof(uint32_t));
     char *b = (char *)base;
     w.ticket = (uint32_t *)b;
@@ -161,7 +161,7 @@ FusedWs fused_ws(const nq_params *p, int32_t q_heads, void *base)
     w.tiles = (keep_count(p) + nq::kFusedTile - 1) / nq::kFusedTile;
     const size_t G = (size_t)(q_heads / p->kv_heads);
     const size_t words = (size_t)w.pairs * w.tiles * 2 * 16 * 4;
-    const size_t t = align_up(2 * sizeof(uint32_t));
+    const size_t t = align_up(nq::kTicketWords * sizeof(uint32_t));
     const size_t v = align_up(words * sizeof(uint32_t));
     const size_t pb = align_up((size_t)w.pairs * w.tiles * G * nq::kPartStride * sizeof(float));
     char *b = (char *)base;
@@ -523,7 +523,7 @@ nq_status nq_decode_attend(const nq_params *p, const int8_t *codes_k, const int8
         const int64_t words = (int64_t)Lc * q_heads * 128;
         clear_error();
         hipLaunchKernelGGL(nq::k_decode_reset, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0,
-                           s, (uint32_t *)out, words, (uint32_t *)out);
+                           s, (uint32_t *)out, words, nullptr);
         return launched("nq_decode_attend");
     }
     const void *ptrs16[] = {codes_k, codes_v, rope_cos, rope_sin};

@@ -31,7 +31,7 @@ struct CodecArgs {
     uint16_t *scales_k, *scales_v; // fp16 bits [Lc][H][n_keep][16]
     void *out_k, *out_v;           // decode outputs [Lc][H][n_keep][128]
     uint32_t *lb_agg, *lb_incl;    // decode look-back words [tiles][16 lanes][4] (see below)
-    uint32_t *lb_ticket;           // [0]: tile ticket counter, [1]: spin-limit error flag
+    uint32_t *lb_ticket;           // kTicketWords: tile ticket counters, spin-limit error flag
     int32_t H, T, layer_begin, n_keep;
     int32_t tiles_per_chain;       // encode tiles (kCodecTile tokens) per chain
     int32_t dec_tiles_per_chain;   // decode tiles (kDecTile tokens) per chain
@@ -78,10 +78,12 @@ __device__ __forceinline__ int lane_group(int l) { return l ^ ((l & 4) ? 3 : 0);
 // of the same operands as in the sequential order, so |values| match it bit for bit.
 __device__ __forceinline__ float group_sign(int g) { return (__popc(g & 15) & 1) ? -1.0f : 1.0f; }
 
+// in-lane stages from h = H0 on
+template <int H0 = 1>
 __device__ __forceinline__ void hadamard_in_lane(float x[8])
 {
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
+    for (int h = H0; h < 8; h <<= 1) {
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             if (!(j & h)) {
@@ -140,39 +142,50 @@ __device__ __forceinline__ uint32_t f16_ceil_bits(float v)
 //   coset D8 + 1/2: nearest half-integers f + sign(e)/2 at distance (1/2 - a) each, sum
 //                   (2 - sum(a) + sum(a^2)), plus 2 min a if sum(f) - #(e < 0) is odd, where
 //                   the coordinate of smallest a moves to the other neighbouring half-integer.
-// The nearer coset wins (D8 on ties). Arg-max/min pack the index into the 3 low bits of |e|,
-// which can only matter between coordinates whose errors differ by a few ulps (a near-tie).
-// Byte work: B0 = 2f + 64 per coordinate; N = [e < 0] per byte (gathered sign bytes); the
-// D8 + 1/2 codes are 2 floor(u) + 65 = B0 + 1 - 2N; parities come from byte sums/popcounts.
+// The nearer coset wins (D8 on ties). Arg-max/min run on one key per coordinate, |e| with its
+// 3 low bits replaced by the index; the index can only decide between coordinates whose
+// errors differ by a few ulps, where the two candidate points are at (nearly) equal distance
+// (a near-tie).
+// Rounding: t = u + M with M = 1.5 * 2^23 + 32 lands where the fp32 spacing is 1, so the add
+// rounds u to an integer with ties to even (M is even: the tie choice is rint's), t = rint(u) + M
+// exactly for |u| < 2^21, and t's low mantissa byte is rint(u) + 32. g = M - t = -rint(u) and
+// e = u + g are exact, with e = +0 whenever u is an integer (-0 included).
+// Byte work: B = f + 32 per coordinate, gathered from the t words; N = [e < 0] per byte
+// (gathered sign bytes); the D8 + 1/2 points are floor(u) + 1/2 = f - N + 1/2; parities come
+// from byte sums / popcounts; the codes c + 64 are 2B (D8) or 2B + 1 (D8 + 1/2).
 __device__ __forceinline__ void e8_nearest_code(const float u[8], uint32_t &w0, uint32_t &w1)
 {
+    constexpr float kMagic = 12582944.0f;   // 1.5 * 2^23 + 32
     float e[8];
-    uint32_t kmax = 0u, kmin = 0xffffffffu, b0 = 0u, b1 = 0u;
+    uint32_t tb[8];
+    uint32_t kmax = 0u, kmin = 0xffffffffu;
     float Sa = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        const float f = __builtin_rintf(u[i]);
-        e[i] = u[i] - f;
-        const uint32_t eb = __float_as_uint(e[i]);
-        // (|e| with its 3 low bits replaced by the index): (eb & 0x7ffffff8) | idx
-        const uint32_t khi = (uint32_t)__builtin_amdgcn_bitop3_b32(eb, 0x7ffffff8u, 7u - (uint32_t)i, 0xEA);
-        const uint32_t klo = (uint32_t)__builtin_amdgcn_bitop3_b32(eb, 0x7ffffff8u, (uint32_t)i, 0xEA);
-        kmax = kmax > khi ? kmax : khi;
-        kmin = kmin < klo ? kmin : klo;
+        const float t = u[i] + kMagic;
+        e[i] = u[i] + (kMagic - t);
+        tb[i] = __float_as_uint(t);
+        // key: (eb & 0x7ffffff8) | i
+        const uint32_t key = (uint32_t)__builtin_amdgcn_bitop3_b32(__float_as_uint(e[i]),
+                                                                   0x7ffffff8u, (uint32_t)i, 0xEA);
+        kmax = kmax > key ? kmax : key;
+        kmin = kmin < key ? kmin : key;
         Sa += __builtin_fabsf(e[i]);
-        const float t = __builtin_fmaf(2.0f, f, 64.0f);
-        if (i < 4) b0 = __builtin_amdgcn_cvt_pk_u8_f32(t, i, b0);
-        else b1 = __builtin_amdgcn_cvt_pk_u8_f32(t, i - 4, b1);
     }
+    // B = f + 32 per byte: byte 0 of each t word
+    uint32_t b0 = __builtin_amdgcn_perm(tb[1], tb[0], 0x0c0c0400u) |
+                  __builtin_amdgcn_perm(tb[3], tb[2], 0x04000c0cu);
+    uint32_t b1 = __builtin_amdgcn_perm(tb[5], tb[4], 0x0c0c0400u) |
+                  __builtin_amdgcn_perm(tb[7], tb[6], 0x04000c0cu);
     // sign bytes of e (byte 3 of each float) gathered into two dwords, then [e < 0] per byte
     const uint32_t g0 = __builtin_amdgcn_perm(__float_as_uint(e[1]), __float_as_uint(e[0]), 0x0c0c0703u) |
                         __builtin_amdgcn_perm(__float_as_uint(e[3]), __float_as_uint(e[2]), 0x07030c0cu);
     const uint32_t g1 = __builtin_amdgcn_perm(__float_as_uint(e[5]), __float_as_uint(e[4]), 0x0c0c0703u) |
                         __builtin_amdgcn_perm(__float_as_uint(e[7]), __float_as_uint(e[6]), 0x07030c0cu);
     const uint32_t n0 = (g0 >> 7) & 0x01010101u, n1 = (g1 >> 7) & 0x01010101u;
-    // sum of bytes = 2 sum(f) + 512: bit 1 is the parity of sum(f)
+    // sum of bytes = sum(f) + 256: bit 0 is the parity of sum(f)
     const uint32_t sb = __builtin_amdgcn_udot4(b0, 0x01010101u, __builtin_amdgcn_udot4(b1, 0x01010101u, 0u, false), false);
-    const int P0 = (int)((sb >> 1) & 1u);
+    const int P0 = (int)(sb & 1u);
     const int P1 = P0 ^ (int)((__popc(n0) + __popc(n1)) & 1u);
     const float amax = __uint_as_float(kmax & ~7u);
     const float amin = __uint_as_float(kmin & ~7u);
@@ -181,59 +194,105 @@ __device__ __forceinline__ void e8_nearest_code(const float u[8], uint32_t &w0, 
     if (P1) dd = __builtin_fmaf(2.0f, amin, dd);
     if (P0) dd = __builtin_fmaf(2.0f, amax, dd - 1.0f);
     const bool half = dd < 0.0f;
-    const int jf = half ? (int)(kmin & 7u) : (int)(7u - (kmax & 7u));
+    const int jf = (int)((half ? kmin : kmax) & 7u);
     const int par = half ? P1 : P0;
     if (half) {
-        b0 = b0 - 2u * n0 + 0x01010101u;   // per byte 2f + 64 - 2[e<0] + 1, never out of [0,255]
-        b1 = b1 - 2u * n1 + 0x01010101u;
+        b0 -= n0;   // floor(u) + 32 per byte (every byte >= 16: no borrow)
+        b1 -= n1;
     }
     if (par) {
-        // D8: re-round toward u (+2 sign(e)); D8 + 1/2: move away from u (-2 sign(e))
+        // D8: re-round toward u (+sign(e)); D8 + 1/2: move away from u (-sign(e))
         const uint32_t neg = ((jf < 4 ? n0 : n1) >> (8 * (jf & 3))) & 1u;
-        int d = neg ? -2 : 2;
+        int d = neg ? -1 : 1;
         if (half) d = -d;
         const uint32_t add = (uint32_t)d << (8 * (jf & 3));
         if (jf < 4) b0 += add; else b1 += add;
     }
-    w0 = b0;
-    w1 = b1;
+    // c + 64 = 2 (y + 32): 2B on D8, 2B + 1 on D8 + 1/2 (bytes stay below 128: no carry)
+    const uint32_t hb = half ? 0x01010101u : 0u;
+    w0 = (b0 << 1) | hb;
+    w1 = (b1 << 1) | hb;
 }
 
-// Encodes one kept token of one chain for this lane's 8 dims. Returns the absolute code bytes
-// (offset +64) and the fp16 scale bits of this lane's group.
-// The codec front end for one kept token (row at position p; X points at this lane's 8 dims
-// of the chain's first row): the fp16 row, for keys the rotary embedding removed at p, then
-// the Hadamard butterflies. x = group_sign(g) times the unnormalised rotated row.
-template <bool IS_KEY>
-__device__ __forceinline__ void front_end(const float *__restrict__ rope_cos,
-                                          const float *__restrict__ rope_sin,
-                                          const uint16_t *__restrict__ X, int p, int g, float x[8])
+// The raw inputs of one kept token for this lane: its 8 fp16 dims and, for keys, the rotary
+// table rows of its position.
+struct TokenIn {
+    u32x4 v;
+    float c[8], s[8];
+};
+
+// this lane's 8 fp16 dims of the row at position p (each K/V row is read once: streamed)
+__device__ __forceinline__ u32x4 load_row(const uint16_t *__restrict__ X, int p)
 {
-    load_f16x8_stream(X + (uint32_t)p * kHeadDim, x);   // each K/V row is read once
-    if (IS_KEY) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(X + (uint32_t)p * kHeadDim));
+}
+
+__device__ __forceinline__ void load_rope(const float *__restrict__ rope_cos,
+                                          const float *__restrict__ rope_sin, int p, int g,
+                                          TokenIn &t)
+{
+    load_f32x8(rope_cos + (size_t)p * 64 + 8 * (g & 7), t.c);
+    load_f32x8(rope_sin + (size_t)p * 64 + 8 * (g & 7), t.s);
+}
+
+template <bool IS_KEY>
+__device__ __forceinline__ void load_token(const float *__restrict__ rope_cos,
+                                           const float *__restrict__ rope_sin,
+                                           const uint16_t *__restrict__ X, int p, int g,
+                                           TokenIn &t)
+{
+    t.v = load_row(X, p);
+    if (IS_KEY) load_rope(rope_cos, rope_sin, p, g, t);
+}
+
+// The codec front end for one kept token (X points at this lane's 8 dims of the chain's first
+// row): the fp16 row, for keys the rotary embedding removed at the token's position, then the
+// Hadamard butterflies. x = group_sign(g) times the unnormalised rotated row.
+template <bool IS_KEY>
+__device__ __forceinline__ void front_end(const TokenIn &t, int g, float x[8])
+{
+    const uint32_t w[4] = {t.v.x, t.v.y, t.v.z, t.v.w};
+    if (!IS_KEY) {
+        // stage h = 1 straight from the fp16 pairs: v_fma_mix_f32 a * 1 + (+-b) converts both
+        // halves exactly and rounds the sum once, as the fp32 add of the converted values
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            asm("v_fma_mix_f32 %0, %2, 1.0, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]\n"
+                "v_fma_mix_f32 %1, %2, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+                : "=&v"(x[2 * k]), "=v"(x[2 * k + 1])
+                : "v"(w[k]));
+        }
+        hadamard_in_lane<2>(x);
+        hadamard_cross_lane(x, g);
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        x[2 * k] = h2f(w[k] & 0xffffu);
+        x[2 * k + 1] = h2f(w[k] >> 16);
+    }
+    {
         // RoPE removal, split-half pairs (i, i + 64) = lanes (g, g ^ 8):
         // x_i = a*C + b*S, x_{i+64} = b*C - a*S with (a, b) = (k_i, k_{i+64}).
-        float c[8], s[8];
-        load_f32x8(rope_cos + (size_t)p * 64 + 8 * (g & 7), c);
-        load_f32x8(rope_sin + (size_t)p * 64 + 8 * (g & 7), s);
         const float sg = g >= 8 ? -1.0f : 1.0f;
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-            const float t1 = x[k] * c[k];
-            const float t2 = lane_xor8(x[k]) * s[k];
+            const float t1 = x[k] * t.c[k];
+            const float t2 = lane_xor8(x[k]) * t.s[k];
             x[k] = __builtin_fmaf(sg, t2, t1);        // t1 +- t2, rounded once
         }
     }
     hadamard_butterflies(x, g);
 }
 
+// Encodes one loaded token for this lane's 8 dims. Returns the absolute code bytes (offset
+// +64) and the fp16 scale bits of this lane's group.
 template <bool IS_KEY>
-__device__ __forceinline__ uint2 encode_token(const CodecArgs &a, const uint16_t *__restrict__ X,
-                                              int p, int g, float rho, float rho_inv,
+__device__ __forceinline__ uint2 encode_token(const TokenIn &t, int g, float rho, float rho_inv,
                                               uint32_t &s16)
 {
     float x[8];
-    front_end<IS_KEY>(a.rope_cos, a.rope_sin, X, p, g, x);
+    front_end<IS_KEY>(t, g, x);
     float amax = 0.0f;
 #pragma unroll
     for (int k = 0; k < 8; k++) amax = fmaxf(amax, __builtin_fabsf(x[k]));
@@ -311,7 +370,9 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
         uint2 hc = zero;
         if (t0 > 0) {
             uint32_t s16;
-            hc = encode_token<IS_KEY>(a, X, s_pos[-1], g, rho, rho_inv, s16);
+            TokenIn t;
+            load_token<IS_KEY>(a.rope_cos, a.rope_sin, X, s_pos[-1], g, t);
+            hc = encode_token<IS_KEY>(t, g, rho, rho_inv, s16);
         }
         s_last[0][g] = hc;
     }
@@ -320,8 +381,10 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
     for (int i = 0; i < kCodecRun; i++) {
         const int j = j0 + i;
         if (j < n_keep) {
+            TokenIn t;
+            load_token<IS_KEY>(a.rope_cos, a.rope_sin, X, s_pos[j - t0], g, t);
             uint32_t s16;
-            const uint2 c = encode_token<IS_KEY>(a, X, s_pos[j - t0], g, rho, rho_inv, s16);
+            const uint2 c = encode_token<IS_KEY>(t, g, rho, rho_inv, s16);
             s_sc[(j - t0) * kGroups + g] = (uint16_t)s16;
             if (i == 0)
                 first = c;
@@ -341,16 +404,19 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
     for (int c = threadIdx.x; c < 2 * nt; c += kCodecThreads) sc[c] = sh.scales[c];
 }
 
-// grid: Lc * 2 * H * tiles_per_chain blocks, XCD-aware order (heads of one token tile adjacent)
+// grid: Lc * 2 * H * tiles_per_chain blocks in XCD-aware order: every head, tensor and layer of
+// one tile index before the next tile index, so the blocks reading rotary rows of nearby
+// positions share an L2
 __global__ __launch_bounds__(kCodecThreads) void k_encode(CodecArgs a)
 {
     const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t Lc = gridDim.x / (2u * a.H * a.tiles_per_chain);
     const int h = id % a.H;
     uint32_t r = id / a.H;
     const int tensor = r & 1;
     r >>= 1;
-    const int tile = r % a.tiles_per_chain;
-    const int lc = r / a.tiles_per_chain;
+    const int lc = r % Lc;
+    const int tile = r / Lc;
     __shared__ EncodeShared sh;
     if (tensor == 0)
         encode_tile<true>(a, lc, h, tile, sh);
@@ -361,8 +427,8 @@ __global__ __launch_bounds__(kCodecThreads) void k_encode(CodecArgs a)
 // ---------------------------------------------------------------------------------------------
 // Decode. Each tile needs the running sum of all earlier deltas of its chain; tiles publish
 // their own byte-wise sum and then their inclusive prefix (single-pass chained scan with
-// decoupled look-back). Tiles take tickets from an atomic counter in launch order, so every
-// tile a tile waits for has already started and makes progress.
+// decoupled look-back). Tiles take tickets from atomic counters in launch order
+// (take_ticket), so every tile a tile waits for has already started and makes progress.
 //
 // Publication needs no memory fence: a tile's 128-byte value is written as 64 words of
 // (tag << 16 | 16 payload bits) with relaxed device-scope atomic stores, tag 1 for the tile
@@ -373,11 +439,34 @@ __global__ __launch_bounds__(kCodecThreads) void k_encode(CodecArgs a)
 // ---------------------------------------------------------------------------------------------
 constexpr uint32_t kSpinLimit = 1u << 26;
 
+// Ticket words: kTicketClasses counters, counter k at word k * kTicketStride (one 128-byte
+// line each), and the spin-limit error flag at word 1.
+constexpr int kTicketClasses = 8;
+constexpr int kTicketStride = 32;
+constexpr int kTicketWords = kTicketClasses * kTicketStride;
+constexpr int kTicketErr = 1;
+
+// Zeroes n words and, when ticket is not null, the kTicketWords ticket words (a launch of at
+// least kTicketWords threads).
 __global__ void k_decode_reset(uint32_t *words, int64_t n, uint32_t *ticket)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) words[i] = 0u;
-    if (i < 2) ticket[i] = 0u;
+    if (ticket && i < kTicketWords) ticket[i] = 0u;
+}
+
+// This block's ticket, taken by one thread. Tickets come from m counters, m the largest power
+// of two <= kTicketClasses that divides `chains`; block b draws from counter b mod m, which
+// deals the tickets congruent to b mod m in the order the blocks arrive (every residue class
+// has as many blocks as tickets). A tile's predecessor, `chains` tickets earlier, is in the
+// same class and was dealt before it, to a block that has started: the oldest unfinished
+// ticket of each class can always proceed, so no wait is circular. A single counter would
+// serialise every block start on one address.
+__device__ __forceinline__ int take_ticket(uint32_t *tickets, uint32_t chains)
+{
+    const uint32_t m = min((uint32_t)kTicketClasses, chains & (0u - chains));
+    const uint32_t k = blockIdx.x & (m - 1u);
+    return (int)(k + m * atomicAdd(tickets + k * kTicketStride, 1u));
 }
 
 __device__ __forceinline__ void lb_publish(uint32_t *base, uint2 v, uint32_t tag)
@@ -685,7 +774,7 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
                IS_KEY ? a.positions + (size_t)lc * n_keep + t0 : nullptr, a.T, sh.delta,
                sh.scale, sh.pos);
     uint2 run = tile_run_base<kDecRun>(sh.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
-                              (size_t)ticket, (size_t)chains, tile, a.lb_ticket + 1);
+                              (size_t)ticket, (size_t)chains, tile, a.lb_ticket + kTicketErr);
     const uint2 *sd = reinterpret_cast<const uint2 *>(sh.delta) + g;   // [token][16 lanes]
     // 4. reconstruct every token of this lane group; the next token's rotary rows are requested
     //    before the current token is computed
@@ -722,10 +811,10 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
 __global__ __launch_bounds__(kCodecThreads) void k_decode(CodecArgs a)
 {
     __shared__ int s_ticket;
-    if (threadIdx.x == 0) s_ticket = (int)atomicAdd(&a.lb_ticket[0], 1u);
+    const int chains = (int)(gridDim.x / (uint32_t)a.dec_tiles_per_chain);
+    if (threadIdx.x == 0) s_ticket = take_ticket(a.lb_ticket, (uint32_t)chains);
     __syncthreads();
     const int ticket = s_ticket;
-    const int chains = (int)(gridDim.x / (uint32_t)a.dec_tiles_per_chain);
     const int tile = ticket / chains;
     uint32_t r = ticket % chains;
     const int h = r % a.H;

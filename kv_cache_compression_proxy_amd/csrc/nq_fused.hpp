@@ -125,10 +125,10 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
 {
     __shared__ int s_ticket;
     __shared__ FusedShared<G> sh;
-    if (threadIdx.x == 0) s_ticket = (int)atomicAdd(&a.lb_ticket[0], 1u);
+    const int pairs = (int)(gridDim.x / (uint32_t)a.tiles);
+    if (threadIdx.x == 0) s_ticket = take_ticket(a.lb_ticket, (uint32_t)pairs);
     __syncthreads();
     const int ticket = s_ticket;
-    const int pairs = (int)(gridDim.x / (uint32_t)a.tiles);
     const int tile = ticket / pairs;
     const int pair = ticket % pairs;
     const int h = pair % a.H, lc = pair / a.H;
@@ -159,7 +159,8 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
                sh.u.t.delta, sh.u.t.scale, sh.pos);
     {
         uint2 run = tile_run_base<kFusedRun>(sh.u.t.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
-                                  2 * (size_t)ticket, 2 * (size_t)pairs, tile, a.lb_ticket + 1);
+                                  2 * (size_t)ticket, 2 * (size_t)pairs, tile,
+                                  a.lb_ticket + kTicketErr);
         const uint2 *sd = reinterpret_cast<const uint2 *>(sh.u.t.delta) + g;
         const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.u.t.scale);
         const int jend = min(nt, jl0 + kFusedRun);
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
     {
         uint2 run = tile_run_base<kFusedRun>(sh.u.t.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
                                   2 * (size_t)ticket + 1, 2 * (size_t)pairs, tile,
-                                  a.lb_ticket + 1);
+                                  a.lb_ticket + kTicketErr);
         const uint2 *sd = reinterpret_cast<const uint2 *>(sh.u.t.delta) + g;
         const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.u.t.scale);
         const int jend = min(nt, jl0 + kFusedRun);

@@ -69,8 +69,10 @@ __device__ void scalar_encode_tile(const ScalarArgs &a, int lc, int h, int tile)
         const int j = tile * kScalarTile + q * kScalarRun + i;
         if (j >= n_keep) break;
         const int p = min(max(pos[j], 0), a.T - 1);
+        TokenIn t;
+        load_token<IS_KEY>(a.rope_cos, a.rope_sin, X, p, g, t);
         float x[8];
-        front_end<IS_KEY>(a.rope_cos, a.rope_sin, X, p, g, x);
+        front_end<IS_KEY>(t, g, x);
         // the normalised rotated row (x * fp32(1/sqrt(128)), lane sign restored: exact)
         float xn[8], ss = 0.0f;
 #pragma unroll
