@@ -94,6 +94,21 @@ ScoreWs score_ws(const nq_params *p, void *base)
 int32_t codec_tiles(const nq_params *p) { return (keep_count(p) + nq::kCodecTile - 1) / nq::kCodecTile; }
 int32_t decode_tiles(const nq_params *p) { return (keep_count(p) + nq::kDecTile - 1) / nq::kDecTile; }
 
+// Per-layer selection: the register-resident kernel when a layer's candidates fit it (up to
+// 32 per thread), else the one that re-reads the scores on every pass.
+constexpr int kSelRegKeys = 32;
+void launch_select(const double *scores, int32_t T, int32_t W, int32_t n_keep, int32_t Lc,
+                   int32_t *positions, hipStream_t s)
+{
+    const int32_t n_cand = T - W > 1 ? T - W - 1 : 0;
+    if (n_cand <= kSelRegKeys * nq::kSelThreads)
+        hipLaunchKernelGGL(nq::k_select_reg<kSelRegKeys>, dim3(Lc), dim3(nq::kSelThreads), 0, s,
+                           scores, T, W, n_keep, positions);
+    else
+        hipLaunchKernelGGL(nq::k_select, dim3(Lc), dim3(nq::kSelThreads), 0, s, scores, T, W,
+                           n_keep, positions);
+}
+
 struct DecodeWs {
     uint32_t *ticket, *agg, *incl;
     size_t bytes;
@@ -347,8 +362,7 @@ nq_status nq_score_evict(const nq_params *p, const void *K, int32_t *positions,
     const int tiles = (T + nq::kScoreTile - 1) / nq::kScoreTile;
     hipLaunchKernelGGL(nq::k_scores, dim3(Lc * tiles), dim3(256), 0, s, K16, w.qbar, H, T,
                        p->window, p->layer_begin, tiles, scores);
-    hipLaunchKernelGGL(nq::k_select, dim3(Lc), dim3(nq::kSelThreads), 0, s, scores, T,
-                       p->window, n_keep, positions);
+    launch_select(scores, T, p->window, n_keep, Lc, positions, s);
     return launched("nq_score_evict");
 }
 
@@ -404,8 +418,7 @@ nq_status nq_score_evict_attn(const nq_params *p, const void *K, const void *Q_o
         hipLaunchKernelGGL(nq::k_attn_finish, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s,
                            a, Lc);
     }
-    hipLaunchKernelGGL(nq::k_select, dim3(Lc), dim3(nq::kSelThreads), 0, s, a.scores, T, W,
-                       n_keep, positions);
+    launch_select(a.scores, T, W, n_keep, Lc, positions, s);
     return launched("nq_score_evict_attn");
 }
 

@@ -297,4 +297,193 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
     }
 }
 
+// ---- selection with the candidate keys held in registers -------------------------------------
+// The same selection as k_select for layers of at most KPT * 1024 candidates: every thread
+// loads its KPT candidates once (positions 1 + tid + 1024 u, u < KPT) and keeps their keys in
+// registers, so the radix passes and the ordered emission read no memory. The emission ranks
+// the kept positions with wave ballots: per chunk u of 1024 consecutive positions, each wave's
+// count goes to LDS, one block scan over the (chunk, wave) counts gives every wave its offset,
+// and a lane adds the kept lanes below it. Ties at the selected key are ranked the same way
+// first (the lowest-positioned ones are kept).
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void k_select_reg(const double *__restrict__ scores,
+                                                            int T, int W, int n_keep,
+                                                            int32_t *__restrict__ positions)
+{
+    constexpr int kWaves = kSelThreads / 64;
+    static_assert(KPT * kWaves <= kSelThreads, "one (chunk, wave) count per thread");
+    __shared__ uint32_t hist[kWaves][256];
+    __shared__ uint32_t s_wave[kWaves];
+    __shared__ uint32_t s_cnt[KPT * kWaves];
+    __shared__ uint64_t s_min[kWaves], s_max[kWaves];
+    __shared__ uint64_t s_prefix, s_mask;
+    __shared__ int s_krem, s_all, s_bits;
+    const int lc = blockIdx.x;
+    const double *s = scores + (size_t)lc * T;
+    int32_t *out = positions + (size_t)lc * n_keep;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c_end = T - W;
+    const int n_cand = c_end > 1 ? c_end - 1 : 0;
+    const int m = n_keep - (T - n_cand);
+    const bool partial = m > 0 && m < n_cand;
+
+    uint64_t key[KPT];
+    {
+        double v[KPT];
+#pragma unroll
+        for (int u = 0; u < KPT; u++) {
+            const int t = 1 + tid + u * kSelThreads;
+            v[u] = t < c_end ? s[t] : 0.0;
+        }
+#pragma unroll
+        for (int u = 0; u < KPT; u++) key[u] = order_key(v[u]);
+    }
+    if (tid == 0) { s_prefix = 0ull; s_mask = 0ull; s_krem = m; s_all = 0; s_bits = 64; }
+    if (partial) {
+        uint64_t kmin = ~0ull, kmax = 0ull;
+#pragma unroll
+        for (int u = 0; u < KPT; u++) {
+            if (1 + tid + u * kSelThreads < c_end) {
+                kmin = key[u] < kmin ? key[u] : kmin;
+                kmax = key[u] > kmax ? key[u] : kmax;
+            }
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint64_t a = __shfl_xor(kmin, d), b = __shfl_xor(kmax, d);
+            kmin = a < kmin ? a : kmin;
+            kmax = b > kmax ? b : kmax;
+        }
+        if (lane == 0) { s_min[wave] = kmin; s_max[wave] = kmax; }
+        __syncthreads();
+        if (tid == 0) {
+            uint64_t lo = s_min[0], hi = s_max[0];
+            for (int w = 1; w < kWaves; w++) {
+                lo = s_min[w] < lo ? s_min[w] : lo;
+                hi = s_max[w] > hi ? s_max[w] : hi;
+            }
+            const int common = lo == hi ? 64 : __clzll((long long)(lo ^ hi));
+            s_bits = 64 - common;
+            s_mask = common == 64 ? ~0ull : (common == 0 ? 0ull : ~0ull << (64 - common));
+            s_prefix = lo & s_mask;
+        }
+    }
+    __syncthreads();
+    if (partial) {
+        for (int top = s_bits; top > 0; top -= 8) {
+            const int shift = top >= 8 ? top - 8 : 0;
+            const uint32_t dmask = top >= 8 ? 255u : ((1u << top) - 1u);
+            for (int i = tid; i < kWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
+            __syncthreads();
+            const uint64_t prefix = s_prefix, mask = s_mask;
+#pragma unroll
+            for (int u = 0; u < KPT; u++)
+                if (1 + tid + u * kSelThreads < c_end && (key[u] & mask) == prefix)
+                    atomicAdd(&hist[wave][(uint32_t)(key[u] >> shift) & dmask], 1u);
+            __syncthreads();
+            if (tid < 256) {
+                uint32_t c = 0;
+                for (int w = 0; w < kWaves; w++) c += hist[w][tid];
+                hist[0][tid] = c;
+            }
+            __syncthreads();
+            if (tid < 64) {
+                const int krem = s_krem;
+                uint32_t c[4], loc = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) { c[i] = hist[0][255 - 4 * tid - i]; loc += c[i]; }
+                uint32_t incl = loc;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const uint32_t o = __shfl_up(incl, d);
+                    if (tid >= d) incl += o;
+                }
+                uint32_t above = incl - loc;
+                if (above < (uint32_t)krem && incl >= (uint32_t)krem) {
+                    for (int i = 0; i < 4; i++) {
+                        if (above + c[i] >= (uint32_t)krem) {
+                            const uint32_t dgt = 255 - 4 * tid - i;
+                            s_prefix = prefix | ((uint64_t)dgt << shift);
+                            s_mask = mask | ((uint64_t)dmask << shift);
+                            s_krem = krem - (int)above;
+                            if (c[i] == (uint32_t)(krem - (int)above)) s_all = 1;
+                            break;
+                        }
+                        above += c[i];
+                    }
+                }
+            }
+            __syncthreads();
+            if (s_all) break;
+        }
+    }
+    const uint64_t prefix = s_prefix, mask = s_mask;
+    const int krem = s_krem;
+    const bool take_all_eq = s_all != 0;
+    const uint64_t below = (1ull << lane) - 1ull;      // lanes under this one
+    // bit u: chunk u's candidate is above the selected key (gt) or equal to it (eq)
+    uint32_t gt = 0u, eq = 0u;
+    static_assert(KPT <= 32, "one flag bit per chunk");
+#pragma unroll
+    for (int u = 0; u < KPT; u++) {
+        const int t = 1 + tid + u * kSelThreads;
+        if (t < c_end) {
+            if (!partial) {
+                if (m > 0) gt |= 1u << u;
+            } else {
+                const uint64_t k = key[u] & mask;
+                if (k > prefix) gt |= 1u << u;
+                else if (k == prefix) eq |= 1u << u;
+            }
+        }
+    }
+    // rank the ties in position order, keep the first krem of them (or all)
+    if (partial && !take_all_eq) {
+#pragma unroll
+        for (int u = 0; u < KPT; u++) {
+            const uint64_t b = __ballot((eq >> u) & 1u);
+            if (lane == 0) s_cnt[u * kWaves + wave] = (uint32_t)__popcll(b);
+        }
+        __syncthreads();
+        uint32_t tot;
+        const uint32_t off = block_excl_scan(tid < KPT * kWaves ? s_cnt[tid] : 0u, s_wave, tot);
+        if (tid < KPT * kWaves) s_cnt[tid] = off;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < KPT; u++) {
+            const uint64_t b = __ballot((eq >> u) & 1u);
+            const uint32_t r = s_cnt[u * kWaves + wave] + (uint32_t)__popcll(b & below);
+            if (((eq >> u) & 1u) && r < (uint32_t)krem) gt |= 1u << u;
+        }
+        __syncthreads();
+    } else {
+        gt |= eq;
+    }
+    // output ranks of the kept candidates; BOS first, the window after the candidates
+#pragma unroll
+    for (int u = 0; u < KPT; u++) {
+        const uint64_t b = __ballot((gt >> u) & 1u);
+        if (lane == 0) s_cnt[u * kWaves + wave] = (uint32_t)__popcll(b);
+    }
+    __syncthreads();
+    uint32_t kept;
+    const uint32_t off = block_excl_scan(tid < KPT * kWaves ? s_cnt[tid] : 0u, s_wave, kept);
+    if (tid < KPT * kWaves) s_cnt[tid] = off;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < KPT; u++) {
+        const uint64_t b = __ballot((gt >> u) & 1u);
+        if ((gt >> u) & 1u) {
+            const uint32_t o = 1u + s_cnt[u * kWaves + wave] + (uint32_t)__popcll(b & below);
+            if (o < (uint32_t)n_keep) out[o] = 1 + tid + u * kSelThreads;
+        }
+    }
+    if (tid == 0 && T > 0 && n_keep > 0) out[0] = 0;
+    const int ws = c_end > 1 ? c_end : 1;               // first window position after BOS
+    for (int t = ws + tid; t < T; t += kSelThreads) {
+        const uint32_t o = 1u + kept + (uint32_t)(t - ws);
+        if (o < (uint32_t)n_keep) out[o] = t;
+    }
+}
+
 }  // namespace nq
