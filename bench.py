@@ -70,7 +70,7 @@ def parse():
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-PHASE_KERNELS = {"score_evict": ("k_window_sum", "k_scores", "k_select"),
+PHASE_KERNELS = {"score_evict": ("k_window_sum", "k_scores", "k_select", "k_select_reg"),
                  "encode": ("k_encode",),
                  "decode": ("k_decode_reset", "k_decode")}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -102,8 +102,10 @@ def summarize_pmc(args, w):
     def per_kernel(d, counter):
         vals = defaultdict(list)
         for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
-            if r["Counter_Name"] == counter:
-                name = r["Kernel_Name"].split("(")[0].replace("nq::", "")
+            if r["Counter_Name"] == counter and ("nq::" in r["Kernel_Name"] or
+                                                 COPY_KERNEL in r["Kernel_Name"]):
+                name = r["Kernel_Name"].split("(")[0].split("<")[0]
+                name = name.replace("void ", "").replace("nq::", "").strip()
                 vals[name].append(float(r["Counter_Value"]))
         return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
 
