@@ -126,15 +126,6 @@ __device__ __forceinline__ void hadamard_butterflies(float x[8], int g)
     hadamard_cross_lane(x, g);
 }
 
-// Smallest fp16 >= v (v > 0 finite), saturating at 65504.
-__device__ __forceinline__ uint32_t f16_ceil_bits(float v)
-{
-    if (v > 65504.0f) return 0x7bffu;
-    uint32_t h = f2h_bits(v);
-    if (h2f(h) < v) h += 1u;
-    return h;
-}
-
 // Nearest E8 point of u (8 floats); returns the codes c = 2y as bytes c + 64 in two dwords.
 // E8 = D8 u (D8 + 1/2) (Conway & Sloane). With f = rint(u), e = u - f, a = |e|:
 //   coset D8:       squared distance sum(a^2), plus (1 - 2 max a) if sum(f) is odd, where the
@@ -304,12 +295,22 @@ __device__ __forceinline__ uint2 encode_token(const TokenIn &t, int g, float rho
     // the correctly rounded one). amax = 0 gives s = 0.
     const float q0 = amax * rho_inv;
     const float rem = __builtin_fmaf(-q0, rho, amax);
-    s16 = f16_ceil_bits(__builtin_fmaf(rem, rho_inv, q0));
+    const float q = __builtin_fmaf(rem, rho_inv, q0);
+    // s = the smallest fp16 >= q, saturating at 65504. In the normal fp16 range, rounding q's
+    // fp32 bits up at bit 13 gives s's fp32 bits (a mantissa carry moves into the exponent);
+    // below 2^-14 (and for q = 0) fp16 steps are 2^-24 apart: s = ceil(q * 2^24) * 2^-24.
+    uint32_t sb32 = min((__float_as_uint(q) + 0x1fffu) & 0xffffe000u, 0x477fe000u);
+    s16 = (sb32 >> 13) - 0x1c000u;
+    if (__builtin_expect(q < 0x1p-14f, 0)) {
+        const float m = __builtin_ceilf(q * 0x1p24f);
+        s16 = (uint32_t)m;
+        sb32 = __float_as_uint(m * 0x1p-24f);
+    }
     // u = x / s up to a few ulps (x * (c * rcp(s)) instead of (x * c) / s): only a point
     // within ~1e-6 of a Voronoi facet can change lattice point, and such points are ties
     // (the butterflies leave group_sign(g) times the row in x; the factor restores the sign).
     // A zero scale means an all-zero group: factor 0 keeps u = 0 (rcp(0) would make NaNs).
-    const float r = __builtin_amdgcn_rcpf(h2f(s16));
+    const float r = __builtin_amdgcn_rcpf(__uint_as_float(sb32));
     const float f = s16 ? (kInvSqrt128 * group_sign(g)) * r : 0.0f;
     float u[8];
 #pragma unroll
