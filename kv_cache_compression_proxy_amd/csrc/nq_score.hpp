@@ -25,11 +25,24 @@ __global__ __launch_bounds__(256) void k_window_sum(const uint16_t *__restrict__
     const int g = threadIdx.x & 15, slot = threadIdx.x >> 4;
     const uint16_t *base = K + ((size_t)(layer_begin + lc) * H + h) * (size_t)T * kHeadDim + 8 * g;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int w = max(0, T - W) + slot; w < T; w += 16) {
-        float x[8];
-        load_f16x8(base + (size_t)w * kHeadDim, x);
+    // 8 rows per thread in flight at once, then their sums (exact in fp64 in any order)
+    for (int w0 = max(0, T - W) + slot; w0 < T; w0 += 16 * 8) {
+        u32x4 v[8];
 #pragma unroll
-        for (int k = 0; k < 8; k++) acc[k] += (double)x[k];
+        for (int r = 0; r < 8; r++) {
+            const int w = w0 + 16 * r;
+            v[r] = w < T ? *reinterpret_cast<const u32x4 *>(base + (size_t)w * kHeadDim)
+                         : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            const uint32_t wd[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                acc[2 * k] += (double)h2f(wd[k] & 0xffffu);
+                acc[2 * k + 1] += (double)h2f(wd[k] >> 16);
+            }
+        }
     }
 #pragma unroll
     for (int k = 0; k < 8; k++) red[slot][8 * g + k] = acc[k];
