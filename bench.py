@@ -35,8 +35,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3])
     ap.add_argument("--cpu-layers", type=int, default=4,
                     help="layers of the workload the CPU oracle baseline processes")
