@@ -106,6 +106,7 @@ __global__ __launch_bounds__(256) void k_scores(const uint16_t *__restrict__ K,
 // order-preserving 64-bit keys finds the m-th best key exactly, then one ordered pass emits BOS,
 // the window, the candidates above that key and the lowest-positioned ones equal to it.
 constexpr int kSelThreads = 1024;
+constexpr int kHistCopies = 16;   // LDS histogram copies of the radix passes (lane mod 16)
 
 __device__ __forceinline__ uint64_t order_key(double d)
 {
@@ -142,7 +143,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
                                                         int32_t *__restrict__ positions)
 {
     constexpr int kWaves = kSelThreads / 64;
-    __shared__ uint32_t hist[kWaves][256];                // one histogram per wave
+    // kHistCopies histogram copies, copy = lane mod kHistCopies: keys crowd into a few digits
+    // on the first passes (sign and exponent bits), and a wave's 64 lanes adding to one LDS
+    // word serialise; with 16 copies at most 4 lanes of an instruction share a word
+    __shared__ uint32_t hist[kHistCopies][256];
     __shared__ uint32_t s_wave[kWaves];
     __shared__ uint64_t s_min[kWaves], s_max[kWaves];
     __shared__ uint64_t s_prefix, s_mask;
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
         for (int top = s_bits; top > 0; top -= 8) {
             const int shift = top >= 8 ? top - 8 : 0;
             const uint32_t dmask = top >= 8 ? 255u : ((1u << top) - 1u);
-            for (int i = tid; i < kWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
+            for (int i = tid; i < kHistCopies * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
             __syncthreads();
             const uint64_t prefix = s_prefix, mask = s_mask;
             // 8 independent loads in flight per thread, then their histogram updates
@@ -218,13 +222,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
                 for (int u = 0; u < 8; u++) {
                     const uint64_t k = order_key(v[u]);
                     if (t0 + u * kSelThreads < c_end && (k & mask) == prefix)
-                        atomicAdd(&hist[wave][(uint32_t)(k >> shift) & dmask], 1u);
+                        atomicAdd(&hist[lane % kHistCopies][(uint32_t)(k >> shift) & dmask], 1u);
                 }
             }
             __syncthreads();
             if (tid < 256) {
                 uint32_t c = 0;
-                for (int w = 0; w < kWaves; w++) c += hist[w][tid];
+                for (int w = 0; w < kHistCopies; w++) c += hist[w][tid];
                 hist[0][tid] = c;
             }
             __syncthreads();
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reg(const double *__rest
 {
     constexpr int kWaves = kSelThreads / 64;
     static_assert(KPT * kWaves <= kSelThreads, "one (chunk, wave) count per thread");
-    __shared__ uint32_t hist[kWaves][256];
+    __shared__ uint32_t hist[kHistCopies][256];   // copies as in k_select
     __shared__ uint32_t s_wave[kWaves];
     __shared__ uint32_t s_cnt[KPT * kWaves];
     __shared__ uint64_t s_min[kWaves], s_max[kWaves];
@@ -386,17 +390,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reg(const double *__rest
         for (int top = s_bits; top > 0; top -= 8) {
             const int shift = top >= 8 ? top - 8 : 0;
             const uint32_t dmask = top >= 8 ? 255u : ((1u << top) - 1u);
-            for (int i = tid; i < kWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
+            for (int i = tid; i < kHistCopies * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
             __syncthreads();
             const uint64_t prefix = s_prefix, mask = s_mask;
 #pragma unroll
             for (int u = 0; u < KPT; u++)
                 if (1 + tid + u * kSelThreads < c_end && (key[u] & mask) == prefix)
-                    atomicAdd(&hist[wave][(uint32_t)(key[u] >> shift) & dmask], 1u);
+                    atomicAdd(&hist[lane % kHistCopies][(uint32_t)(key[u] >> shift) & dmask], 1u);
             __syncthreads();
             if (tid < 256) {
                 uint32_t c = 0;
-                for (int w = 0; w < kWaves; w++) c += hist[w][tid];
+                for (int w = 0; w < kHistCopies; w++) c += hist[w][tid];
                 hist[0][tid] = c;
             }
             __syncthreads();
