@@ -390,19 +390,23 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
             if (i == 0)
                 first = c;
             else
-                *reinterpret_cast<uint2 *>(codes + (size_t)j * kHeadDim) = delta_code(c, prev);
+                store_stream(codes + (size_t)j * kHeadDim, delta_code(c, prev));
             prev = c;
         }
     }
     s_last[q + 1][g] = prev;
     __syncthreads();
     if (j0 < n_keep)
-        *reinterpret_cast<uint2 *>(codes + (size_t)j0 * kHeadDim) = delta_code(first, s_last[q][g]);
-    // the tile's scales: 32 bytes per token, written as 16-byte chunks
+        store_stream(codes + (size_t)j0 * kHeadDim, delta_code(first, s_last[q][g]));
+    // the tile's scales: 32 bytes per token, written as 16-byte chunks past the caches
     const int nt = min(kCodecTile, n_keep - t0);
     uint4 *sc = reinterpret_cast<uint4 *>((IS_KEY ? a.scales_k : a.scales_v) +
                                           (chain * (size_t)n_keep + t0) * kGroups);
-    for (int c = threadIdx.x; c < 2 * nt; c += kCodecThreads) sc[c] = sh.scales[c];
+    for (int c = threadIdx.x; c < 2 * nt; c += kCodecThreads) {
+        const uint4 v = sh.scales[c];
+        const u32x4 w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(sc + c));
+    }
 }
 
 // grid: Lc * 2 * H * tiles_per_chain blocks in XCD-aware order: every head, tensor and layer of

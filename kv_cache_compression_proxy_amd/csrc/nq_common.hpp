@@ -28,6 +28,7 @@ __device__ __forceinline__ uint16_t f2h_bits(float x)   // round to nearest even
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -50,6 +51,13 @@ __device__ __forceinline__ void load_f16x8(const uint16_t *__restrict__ p, float
 }
 
 // the same for data read once: a non-temporal load does not keep the line in the caches
+// 8 bytes stored past the caches (outputs written once and not read back by the kernel)
+__device__ __forceinline__ void store_stream(void *p, uint2 v)
+{
+    const u32x2 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2 *>(p));
+}
+
 __device__ __forceinline__ void load_f16x8_stream(const uint16_t *__restrict__ p, float x[8])
 {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
