@@ -236,9 +236,9 @@ __device__ __forceinline__ void load_token(const float *__restrict__ rope_cos,
     if (IS_KEY) load_rope(rope_cos, rope_sin, p, g, t);
 }
 
-// The codec front end for one kept token (X points at this lane's 8 dims of the chain's first
-// row): the fp16 row, for keys the rotary embedding removed at the token's position, then the
-// Hadamard butterflies. x = group_sign(g) times the unnormalised rotated row.
+// The codec front end for one kept token loaded into t: the fp16 row, for keys the rotary
+// embedding removed at the token's position, then the Hadamard butterflies. x = group_sign(g)
+// times the unnormalised rotated row.
 template <bool IS_KEY>
 __device__ __forceinline__ void front_end(const TokenIn &t, int g, float x[8])
 {
