@@ -118,6 +118,10 @@ EDGE = [
     ("small-keep", 1, 8, 40, 3, 900, 3, 2, 1e4, 0, 1),
     ("single-head-long", 1, 1, 20000, 128, 600, 3, 2, 1e4, 0, 1),
     ("tile-exact", 1, 4, 640, 0, 600, 3, 2, 1e4, 0, 1),       # n_keep = 256
+    # the selection's two kernels: 32768 candidates (the most the register-resident one
+    # takes) and 32769 (the one that re-reads the scores)
+    ("select-32768-candidates", 1, 1, 33025, 256, 600, 3, 2, 1e4, 0, 1),
+    ("select-32769-candidates", 1, 1, 33026, 256, 600, 3, 2, 1e4, 0, 1),
 ]
 
 
