@@ -138,33 +138,120 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *s_wave
     return before + incl - v;
 }
 
+// LDS state of one layer's selection. The radix histograms come in kHistCopies copies, copy =
+// lane mod kHistCopies: keys crowd into a few digits on the first passes (sign and exponent
+// bits), and a wave's 64 lanes adding to one LDS word serialise; with 16 copies at most 4
+// lanes of an instruction share a word.
+struct SelectShared {
+    uint32_t hist[kHistCopies][256];
+    uint32_t wave_sum[kSelThreads / 64];
+    uint64_t wave_min[kSelThreads / 64], wave_max[kSelThreads / 64];
+    uint64_t prefix, mask;   // bits of the m-th best key resolved so far
+    int krem;                // rank of that key among the keys matching prefix/mask
+    int all;                 // the whole matching bucket is kept
+    int bits;                // bits left to resolve
+};
+
+// Radix state from every thread's smallest and largest candidate key: the bits shared by all
+// candidates (the common prefix of the extremes) need no pass. Ends with a barrier.
+__device__ __forceinline__ void sel_init_prefix(SelectShared &sh, uint64_t kmin, uint64_t kmax)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t a = __shfl_xor(kmin, d), b = __shfl_xor(kmax, d);
+        kmin = a < kmin ? a : kmin;
+        kmax = b > kmax ? b : kmax;
+    }
+    if (lane == 0) { sh.wave_min[wave] = kmin; sh.wave_max[wave] = kmax; }
+    __syncthreads();
+    if (tid == 0) {
+        uint64_t lo = sh.wave_min[0], hi = sh.wave_max[0];
+        for (int w = 1; w < kSelThreads / 64; w++) {
+            lo = sh.wave_min[w] < lo ? sh.wave_min[w] : lo;
+            hi = sh.wave_max[w] > hi ? sh.wave_max[w] : hi;
+        }
+        const int common = lo == hi ? 64 : __clzll((long long)(lo ^ hi));
+        sh.bits = 64 - common;
+        sh.mask = common == 64 ? ~0ull : (common == 0 ? 0ull : ~0ull << (64 - common));
+        sh.prefix = lo & sh.mask;
+    }
+    __syncthreads();
+}
+
+// Clears the histogram copies. Ends with a barrier.
+__device__ __forceinline__ void sel_clear_hist(SelectShared &sh)
+{
+    for (int i = threadIdx.x; i < kHistCopies * 256; i += kSelThreads) (&sh.hist[0][0])[i] = 0u;
+    __syncthreads();
+}
+
+// One radix digit: key k (matching the pass's prefix/mask) counted in its lane's copy
+__device__ __forceinline__ void sel_count(SelectShared &sh, uint64_t k, int shift, uint32_t dmask)
+{
+    atomicAdd(&sh.hist[(threadIdx.x & 63) % kHistCopies][(uint32_t)(k >> shift) & dmask], 1u);
+}
+
+// After a pass has counted its keys: sums the copies, finds the digit that holds the krem-th
+// largest key and narrows prefix/mask/krem to it (all = 1 when the whole bucket is kept).
+// Starts and ends with a barrier.
+__device__ __forceinline__ void sel_pick_digit(SelectShared &sh, int shift, uint32_t dmask,
+                                               uint64_t prefix, uint64_t mask)
+{
+    const int tid = threadIdx.x;
+    __syncthreads();
+    if (tid < 256) {
+        uint32_t c = 0;
+        for (int w = 0; w < kHistCopies; w++) c += sh.hist[w][tid];
+        sh.hist[0][tid] = c;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // lane L covers digits 255-4L .. 252-4L (descending)
+        const int krem = sh.krem;
+        uint32_t c[4], loc = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) { c[i] = sh.hist[0][255 - 4 * tid - i]; loc += c[i]; }
+        uint32_t incl = loc;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t o = __shfl_up(incl, d);
+            if (tid >= d) incl += o;
+        }
+        uint32_t above = incl - loc;               // keys in higher digits
+        if (above < (uint32_t)krem && incl >= (uint32_t)krem) {
+            for (int i = 0; i < 4; i++) {
+                if (above + c[i] >= (uint32_t)krem) {
+                    const uint32_t dgt = 255 - 4 * tid - i;
+                    sh.prefix = prefix | ((uint64_t)dgt << shift);
+                    sh.mask = mask | ((uint64_t)dmask << shift);
+                    sh.krem = krem - (int)above;
+                    if (c[i] == (uint32_t)(krem - (int)above)) sh.all = 1;
+                    break;
+                }
+                above += c[i];
+            }
+        }
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict__ scores, int T,
                                                         int W, int n_keep,
                                                         int32_t *__restrict__ positions)
 {
-    constexpr int kWaves = kSelThreads / 64;
-    // kHistCopies histogram copies, copy = lane mod kHistCopies: keys crowd into a few digits
-    // on the first passes (sign and exponent bits), and a wave's 64 lanes adding to one LDS
-    // word serialise; with 16 copies at most 4 lanes of an instruction share a word
-    __shared__ uint32_t hist[kHistCopies][256];
-    __shared__ uint32_t s_wave[kWaves];
-    __shared__ uint64_t s_min[kWaves], s_max[kWaves];
-    __shared__ uint64_t s_prefix, s_mask;
-    __shared__ int s_krem, s_all, s_bits;
+    __shared__ SelectShared sh;
     const int lc = blockIdx.x;
     const double *s = scores + (size_t)lc * T;
     int32_t *out = positions + (size_t)lc * n_keep;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int c_end = T - W;
     const int n_cand = c_end > 1 ? c_end - 1 : 0;
     const int m = n_keep - (T - n_cand);
     const bool partial = m > 0 && m < n_cand;
 
-    if (tid == 0) { s_prefix = 0ull; s_mask = 0ull; s_krem = m; s_all = 0; s_bits = 64; }
+    if (tid == 0) { sh.prefix = 0ull; sh.mask = 0ull; sh.krem = m; sh.all = 0; sh.bits = 64; }
     if (partial) {
-        // bits shared by every candidate key (the common prefix of the smallest and largest
-        // key) need no radix pass: random scores share sign and high exponent bits, which
-        // would otherwise send every key to one histogram bucket
         uint64_t kmin = ~0ull, kmax = 0ull;
         for (int t0 = 1 + tid; t0 < c_end; t0 += 8 * kSelThreads) {
             double v[8];
@@ -182,34 +269,15 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
                 }
             }
         }
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint64_t a = __shfl_xor(kmin, d), b = __shfl_xor(kmax, d);
-            kmin = a < kmin ? a : kmin;
-            kmax = b > kmax ? b : kmax;
-        }
-        if (lane == 0) { s_min[wave] = kmin; s_max[wave] = kmax; }
-        __syncthreads();
-        if (tid == 0) {
-            uint64_t lo = s_min[0], hi = s_max[0];
-            for (int w = 1; w < kWaves; w++) {
-                lo = s_min[w] < lo ? s_min[w] : lo;
-                hi = s_max[w] > hi ? s_max[w] : hi;
-            }
-            const int common = lo == hi ? 64 : __clzll((long long)(lo ^ hi));
-            s_bits = 64 - common;                           // bits left to resolve
-            s_mask = common == 64 ? ~0ull : (common == 0 ? 0ull : ~0ull << (64 - common));
-            s_prefix = lo & s_mask;
-        }
+        sel_init_prefix(sh, kmin, kmax);
     }
     __syncthreads();
     if (partial) {
-        for (int top = s_bits; top > 0; top -= 8) {
+        for (int top = sh.bits; top > 0; top -= 8) {
             const int shift = top >= 8 ? top - 8 : 0;
             const uint32_t dmask = top >= 8 ? 255u : ((1u << top) - 1u);
-            for (int i = tid; i < kHistCopies * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
-            __syncthreads();
-            const uint64_t prefix = s_prefix, mask = s_mask;
+            sel_clear_hist(sh);
+            const uint64_t prefix = sh.prefix, mask = sh.mask;
             // 8 independent loads in flight per thread, then their histogram updates
             for (int t0 = 1 + tid; t0 < c_end; t0 += 8 * kSelThreads) {
                 double v[8];
@@ -222,51 +290,16 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
                 for (int u = 0; u < 8; u++) {
                     const uint64_t k = order_key(v[u]);
                     if (t0 + u * kSelThreads < c_end && (k & mask) == prefix)
-                        atomicAdd(&hist[lane % kHistCopies][(uint32_t)(k >> shift) & dmask], 1u);
+                        sel_count(sh, k, shift, dmask);
                 }
             }
-            __syncthreads();
-            if (tid < 256) {
-                uint32_t c = 0;
-                for (int w = 0; w < kHistCopies; w++) c += hist[w][tid];
-                hist[0][tid] = c;
-            }
-            __syncthreads();
-            if (tid < 64) {
-                // lane L covers digits 255-4L .. 252-4L (descending); find the digit holding
-                // the krem-th largest key
-                const int krem = s_krem;
-                uint32_t c[4], loc = 0;
-#pragma unroll
-                for (int i = 0; i < 4; i++) { c[i] = hist[0][255 - 4 * tid - i]; loc += c[i]; }
-                uint32_t incl = loc;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const uint32_t o = __shfl_up(incl, d);
-                    if (tid >= d) incl += o;
-                }
-                uint32_t above = incl - loc;               // keys in higher digits
-                if (above < (uint32_t)krem && incl >= (uint32_t)krem) {
-                    for (int i = 0; i < 4; i++) {
-                        if (above + c[i] >= (uint32_t)krem) {
-                            const uint32_t dgt = 255 - 4 * tid - i;
-                            s_prefix = prefix | ((uint64_t)dgt << shift);
-                            s_mask = mask | ((uint64_t)dmask << shift);
-                            s_krem = krem - (int)above;
-                            if (c[i] == (uint32_t)(krem - (int)above)) s_all = 1;
-                            break;
-                        }
-                        above += c[i];
-                    }
-                }
-            }
-            __syncthreads();
-            if (s_all) break;                              // the whole bucket is kept
+            sel_pick_digit(sh, shift, dmask, prefix, mask);
+            if (sh.all) break;                             // the whole bucket is kept
         }
     }
-    const uint64_t prefix = s_prefix, mask = s_mask;
-    const int krem = s_krem;
-    const bool take_all_eq = s_all != 0;
+    const uint64_t prefix = sh.prefix, mask = sh.mask;
+    const int krem = sh.krem;
+    const bool take_all_eq = sh.all != 0;
     // ordered emission: chunks of 4 consecutive positions per thread
     uint32_t eq_base = 0, out_base = 0;
     for (int t0 = 0; t0 < T; t0 += 4 * kSelThreads) {
@@ -291,7 +324,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
             else if (k == prefix) eqf |= 1u << i;
         }
         uint32_t eq_tot;
-        const uint32_t eq_before = block_excl_scan(__builtin_popcount(eqf), s_wave, eq_tot);
+        const uint32_t eq_before = block_excl_scan(__builtin_popcount(eqf), sh.wave_sum, eq_tot);
         uint32_t r = eq_base + eq_before;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -303,7 +336,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double *__restrict
         }
         eq_base += eq_tot;
         uint32_t k_tot;
-        uint32_t o = out_base + block_excl_scan(__builtin_popcount(keepf), s_wave, k_tot);
+        uint32_t o = out_base + block_excl_scan(__builtin_popcount(keepf), sh.wave_sum, k_tot);
 #pragma unroll
         for (int i = 0; i < 4; i++)
             if (keepf & (1u << i)) {
@@ -329,12 +362,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reg(const double *__rest
 {
     constexpr int kWaves = kSelThreads / 64;
     static_assert(KPT * kWaves <= kSelThreads, "one (chunk, wave) count per thread");
-    __shared__ uint32_t hist[kHistCopies][256];   // copies as in k_select
-    __shared__ uint32_t s_wave[kWaves];
+    __shared__ SelectShared sh;
     __shared__ uint32_t s_cnt[KPT * kWaves];
-    __shared__ uint64_t s_min[kWaves], s_max[kWaves];
-    __shared__ uint64_t s_prefix, s_mask;
-    __shared__ int s_krem, s_all, s_bits;
     const int lc = blockIdx.x;
     const double *s = scores + (size_t)lc * T;
     int32_t *out = positions + (size_t)lc * n_keep;
@@ -355,7 +384,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reg(const double *__rest
 #pragma unroll
         for (int u = 0; u < KPT; u++) key[u] = order_key(v[u]);
     }
-    if (tid == 0) { s_prefix = 0ull; s_mask = 0ull; s_krem = m; s_all = 0; s_bits = 64; }
+    if (tid == 0) { sh.prefix = 0ull; sh.mask = 0ull; sh.krem = m; sh.all = 0; sh.bits = 64; }
     if (partial) {
         uint64_t kmin = ~0ull, kmax = 0ull;
 #pragma unroll
@@ -365,78 +394,26 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reg(const double *__rest
                 kmax = key[u] > kmax ? key[u] : kmax;
             }
         }
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint64_t a = __shfl_xor(kmin, d), b = __shfl_xor(kmax, d);
-            kmin = a < kmin ? a : kmin;
-            kmax = b > kmax ? b : kmax;
-        }
-        if (lane == 0) { s_min[wave] = kmin; s_max[wave] = kmax; }
-        __syncthreads();
-        if (tid == 0) {
-            uint64_t lo = s_min[0], hi = s_max[0];
-            for (int w = 1; w < kWaves; w++) {
-                lo = s_min[w] < lo ? s_min[w] : lo;
-                hi = s_max[w] > hi ? s_max[w] : hi;
-            }
-            const int common = lo == hi ? 64 : __clzll((long long)(lo ^ hi));
-            s_bits = 64 - common;
-            s_mask = common == 64 ? ~0ull : (common == 0 ? 0ull : ~0ull << (64 - common));
-            s_prefix = lo & s_mask;
-        }
+        sel_init_prefix(sh, kmin, kmax);
     }
     __syncthreads();
     if (partial) {
-        for (int top = s_bits; top > 0; top -= 8) {
+        for (int top = sh.bits; top > 0; top -= 8) {
             const int shift = top >= 8 ? top - 8 : 0;
             const uint32_t dmask = top >= 8 ? 255u : ((1u << top) - 1u);
-            for (int i = tid; i < kHistCopies * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
-            __syncthreads();
-            const uint64_t prefix = s_prefix, mask = s_mask;
+            sel_clear_hist(sh);
+            const uint64_t prefix = sh.prefix, mask = sh.mask;
 #pragma unroll
             for (int u = 0; u < KPT; u++)
                 if (1 + tid + u * kSelThreads < c_end && (key[u] & mask) == prefix)
-                    atomicAdd(&hist[lane % kHistCopies][(uint32_t)(key[u] >> shift) & dmask], 1u);
-            __syncthreads();
-            if (tid < 256) {
-                uint32_t c = 0;
-                for (int w = 0; w < kHistCopies; w++) c += hist[w][tid];
-                hist[0][tid] = c;
-            }
-            __syncthreads();
-            if (tid < 64) {
-                const int krem = s_krem;
-                uint32_t c[4], loc = 0;
-#pragma unroll
-                for (int i = 0; i < 4; i++) { c[i] = hist[0][255 - 4 * tid - i]; loc += c[i]; }
-                uint32_t incl = loc;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const uint32_t o = __shfl_up(incl, d);
-                    if (tid >= d) incl += o;
-                }
-                uint32_t above = incl - loc;
-                if (above < (uint32_t)krem && incl >= (uint32_t)krem) {
-                    for (int i = 0; i < 4; i++) {
-                        if (above + c[i] >= (uint32_t)krem) {
-                            const uint32_t dgt = 255 - 4 * tid - i;
-                            s_prefix = prefix | ((uint64_t)dgt << shift);
-                            s_mask = mask | ((uint64_t)dmask << shift);
-                            s_krem = krem - (int)above;
-                            if (c[i] == (uint32_t)(krem - (int)above)) s_all = 1;
-                            break;
-                        }
-                        above += c[i];
-                    }
-                }
-            }
-            __syncthreads();
-            if (s_all) break;
+                    sel_count(sh, key[u], shift, dmask);
+            sel_pick_digit(sh, shift, dmask, prefix, mask);
+            if (sh.all) break;
         }
     }
-    const uint64_t prefix = s_prefix, mask = s_mask;
-    const int krem = s_krem;
-    const bool take_all_eq = s_all != 0;
+    const uint64_t prefix = sh.prefix, mask = sh.mask;
+    const int krem = sh.krem;
+    const bool take_all_eq = sh.all != 0;
     const uint64_t below = (1ull << lane) - 1ull;      // lanes under this one
     // bit u: chunk u's candidate is above the selected key (gt) or equal to it (eq)
     uint32_t gt = 0u, eq = 0u;
@@ -463,7 +440,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reg(const double *__rest
         }
         __syncthreads();
         uint32_t tot;
-        const uint32_t off = block_excl_scan(tid < KPT * kWaves ? s_cnt[tid] : 0u, s_wave, tot);
+        const uint32_t off = block_excl_scan(tid < KPT * kWaves ? s_cnt[tid] : 0u, sh.wave_sum, tot);
         if (tid < KPT * kWaves) s_cnt[tid] = off;
         __syncthreads();
 #pragma unroll
@@ -484,7 +461,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reg(const double *__rest
     }
     __syncthreads();
     uint32_t kept;
-    const uint32_t off = block_excl_scan(tid < KPT * kWaves ? s_cnt[tid] : 0u, s_wave, kept);
+    const uint32_t off = block_excl_scan(tid < KPT * kWaves ? s_cnt[tid] : 0u, sh.wave_sum, kept);
     if (tid < KPT * kWaves) s_cnt[tid] = off;
     __syncthreads();
 #pragma unroll
