@@ -176,3 +176,53 @@ def test_decode_of_oracle_codes():
     rv, _ = recon_ratio(Vo[0].cpu().numpy(), Vh, enc["scales_v"], zero)
     say(f"[decode-oracle-codes] recon k {rk:.3g} v {rv:.3g}")
     assert rk <= RECON_TOL and rv <= RECON_TOL
+
+
+def special_rows(H, T, seed):
+    """K, V [H, T, 128] fp16 whose token rows take the codec's special paths: all-zero rows
+    (zero scales), rows of fp16 subnormals (scales below 2^-14), rows at +-65504 (saturated
+    scales, clamped u), one-hot rows and small-integer rows (exact lattice ties), groups zero in
+    one half of the row, and Gaussian rows between them."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for kind in range(2):
+        X = rng.standard_normal((H, T, 128)).astype(np.float32)
+        seg = T // 8
+        X[:, 1:seg] = 0.0
+        X[:, seg:2 * seg] = rng.choice([-1.0, 1.0], (H, seg, 128)) * 2.0 ** -20
+        X[:, 2 * seg:3 * seg] = rng.choice([-1.0, 1.0], (H, seg, 128)) * 65504.0
+        # rows the Hadamard rotation gathers into one dim (keys: constant after the rotary
+        # embedding is removed at the row's position)
+        if kind == 0:
+            C, S = oracle.rope_table(T, 1e4)
+            t = np.arange(2 * seg, 2 * seg + seg // 2)
+            a = 46000.0                                  # a * (C + S) stays within fp16
+            X[:, t, :64] = a * (C[t] - S[t])
+            X[:, t, 64:] = a * (S[t] + C[t])
+        else:
+            X[:, 2 * seg:2 * seg + seg // 2] = 65504.0
+        X[:, 3 * seg:4 * seg] = 0.0
+        for h in range(H):
+            for t in range(3 * seg, 4 * seg):
+                X[h, t, (t * 7 + h) % 128] = 1.0
+        X[:, 4 * seg:5 * seg] = rng.integers(-2, 3, (H, seg, 128))
+        X[:, 5 * seg:6 * seg, :64] = 0.0
+        out.append(X.astype(np.float16))
+    return out[0], out[1]
+
+
+@pytest.mark.parametrize("bits_k,bits_v", [(3, 2), (4, 4), (2, 3)])
+def test_special_rows(bits_k, bits_v):
+    H, T, W = 2, 800, 16
+    K, V = special_rows(H, T, 7 + bits_k)
+    p = nq.make_params(1, H, T, W, 0, bits_k, bits_v, 1e4)     # no eviction: every row coded
+    dev = "cuda"
+    run = GpuRun(p, torch.from_numpy(K[None]).to(dev), torch.from_numpy(V[None]).to(dev))
+    assert run.lookback_error() == 0
+    Ct, St = oracle.rope_table(T, 1e4)
+    st = check_layer(None, p, run, K, V, 0, Ct, St)
+    say(f"[special] K{bits_k}V{bits_v}: {st}")
+    # the special scale paths were taken, in keys and in values
+    for sc in (run.scales_k[0], run.scales_v[0]):
+        s16 = sc.cpu().numpy().view(np.uint16)
+        assert (s16 == 0).any() and (s16 == 0x7BFF).any() and ((s16 > 0) & (s16 < 0x0400)).any()
