@@ -203,7 +203,7 @@ nq_status nq_lloyd_max_table(int32_t bits, double *levels, double *thresholds);
 /* The codec's front end (keys rotated back by their position, normalised Hadamard rotation)
  * with a per-coordinate Lloyd-Max quantizer in place of the E8 step, at bits_k / bits_v bits:
  * per 8-float group the fp16 scale s = RMS of the group (fp32, squares added in dim order,
- * rounded to nearest fp16) and per coordinate the index of u = x / s in the table (number of
+ * rounded to nearest fp16, saturating at 65504) and per coordinate the index of u = x / s in the table (number of
  * thresholds strictly below u; an all-zero group gets 2^(b-1)). No delta coding.
  *   idx_k, idx_v        uint8 [L_c][H][n_keep][128] out (8-byte aligned)
  *   scales_k, scales_v  fp16 [L_c][H][n_keep][16] out

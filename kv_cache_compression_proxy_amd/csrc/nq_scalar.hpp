@@ -4,8 +4,8 @@
 // coordinate (page "Lloyd-Max量化": sections "量化过程详解" -- alternate nearest-level assignment
 // and centroid updates, then quantize by table lookup -- and "3-bit量化的设计选择").
 //
-// Group scale: the fp16 (nearest even) of the group's RMS, sqrt(sum x^2 / 8) in fp32 with the
-// squares added in dim order; index = number of thresholds strictly below u = x / s (fp32
+// Group scale: the fp16 (nearest even, saturating at 65504) of the group's RMS, sqrt(sum x^2 / 8)
+// in fp32 with the squares added in dim order; index = number of thresholds strictly below u = x / s (fp32
 // division); an all-zero group takes index 2^(b-1). Indices are stored one per byte, with no
 // delta coding. Decode: x = s * level[index], the inverse transform, RoPE at the stored
 // position. Tables come from the host (computed once per bit width by the Lloyd-Max iteration).
@@ -80,7 +80,7 @@ __device__ void scalar_encode_tile(const ScalarArgs &a, int lc, int h, int tile)
             xn[k] = (x[k] * kInvSqrt128) * sg;
             ss = ss + xn[k] * xn[k];
         }
-        const uint32_t s16 = f2h_bits(sqrtf(ss * 0.125f));
+        const uint32_t s16 = min(f2h_bits(sqrtf(ss * 0.125f)), 0x7bffu);   // saturating
         const float s = h2f(s16);
         uint2 id;
         if (bits == 2) id = scalar_indices<3>(xn, s, a.thr[tn], half);

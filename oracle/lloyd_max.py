@@ -10,8 +10,9 @@ assignment and centroid updates until they converge, then quantize by table look
 "3-bit量化的设计选择" section fixes the 3-bit budget. After the rotation the coordinates are
 close to Gaussian, so the tables are those of N(0, 1) and need no data.
 
-Readings (the pages leave them open): the group scale is the fp16 (round to nearest even) of
-the group's RMS, s = sqrt(sum(x_i^2) / 8) in fp32 with the squares added in dim order; a
+Readings (the pages leave them open): the group scale is the fp16 (round to nearest even,
+saturating at 65504 so that it stays finite) of the group's RMS, s = sqrt(sum(x_i^2) / 8) in
+fp32 with the squares added in dim order; a
 coordinate's index is the number of thresholds strictly below u = x / s (fp32 division, fp32
 thresholds), so a value on a threshold takes the lower cell; an all-zero group (s = 0) takes
 index 2^(b-1) everywhere (its reconstruction is 0 whatever the index).
@@ -94,7 +95,7 @@ def quantize_group(x8: np.ndarray, bits: int):
     for v in x8.astype(np.float32):
         ss = np.float32(ss + np.float32(v * v))
     s32 = np.float32(np.sqrt(np.float32(ss * np.float32(0.125))))
-    s16 = f2h_rne(float(s32))
+    s16 = min(f2h_rne(float(s32)), 0x7BFF)   # saturating: an RMS above 65504 keeps 65504
     s = np.float32(h2f(s16))
     near = False
     # scale near-tie: fp32 RMS within 1e-6 relative of an fp16 rounding boundary

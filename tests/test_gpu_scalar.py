@@ -22,11 +22,11 @@ pytestmark = pytest.mark.gpu
 RECON_TOL = 1e-5
 
 
-def run(T, W, e, bits_k, bits_v, layer=0):
+def run(T, W, e, bits_k, bits_v, layer=0, rows=None):
     w = kvsynth.workload(0).with_(tokens=T, window=W, evict_permille=e, bits_k=bits_k,
                                   bits_v=bits_v)
-    H = w.kv_heads
-    K_l, V_l = kvsynth.layer_kv(w, layer)
+    K_l, V_l = kvsynth.layer_kv(w, layer) if rows is None else rows
+    H = K_l.shape[0]
     Ct, St = oracle.rope_table(T, w.rope_base)
     pos, _, _ = oracle.select_layer(oracle.layer_scores(K_l, W), W, e)
     ora = lm.encode_layer(K_l, V_l, pos, Ct, St, bits_k, bits_v)
@@ -82,3 +82,13 @@ def run(T, W, e, bits_k, bits_v, layer=0):
 def test_scalar_parity(T, W, e, bk, bv):
     st = run(T, W, e, bk, bv)
     say(f"[scalar] T={T} W={W} e={e} K{bk}V{bv}: {st}")
+
+
+@pytest.mark.parametrize("bk,bv", [(3, 2), (2, 4)])
+def test_scalar_special_rows(bk, bv):
+    """Crafted rows (all-zero, fp16-subnormal, +-65504 and rows the rotation gathers into one
+    dim, one-hot, small integers): zero, tiny and saturated RMS scales."""
+    from test_gpu_parity import special_rows
+    T = 800
+    st = run(T, 16, 0, bk, bv, rows=special_rows(2, T, 11 + bk))
+    say(f"[scalar special] K{bk}V{bv}: {st}")

@@ -69,6 +69,11 @@ def test_group_quantization_known_answers():
     assert np.array_equal(i_got, idx)
     z16, z_idx, _ = quantize_group(np.zeros(8, np.float32), 2)
     assert z16 == 0 and np.all(z_idx == 2)
+    # an RMS beyond the fp16 range keeps the largest finite scale; u then lies beyond every
+    # threshold in magnitude, so the indices are the outermost cells
+    big = np.array([2e5, -2e5, 2e5, -2e5, 2e5, -2e5, 2e5, -2e5], np.float32)
+    b16, b_idx, _ = quantize_group(big, 3)
+    assert b16 == 0x7BFF and list(b_idx) == [7, 0, 7, 0, 7, 0, 7, 0]
 
 
 def test_decode_inverts_the_rotation():
