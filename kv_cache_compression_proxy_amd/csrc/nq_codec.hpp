@@ -30,7 +30,7 @@ struct CodecArgs {
     int8_t *codes_k, *codes_v;     // [Lc][H][n_keep][128]
     uint16_t *scales_k, *scales_v; // fp16 bits [Lc][H][n_keep][16]
     void *out_k, *out_v;           // decode outputs [Lc][H][n_keep][128]
-    uint32_t *lb_agg, *lb_incl;    // decode look-back words [tiles][16 lanes][4] (see below)
+    uint32_t *lb_agg, *lb_incl;    // decode look-back words [tiles][4][16 lanes] (see below)
     uint32_t *lb_ticket;           // kTicketWords: tile ticket counters, spin-limit error flag
     int32_t H, T, layer_begin, n_keep;
     int32_t tiles_per_chain;       // encode tiles (kCodecTile tokens) per chain
@@ -474,22 +474,26 @@ __device__ __forceinline__ int take_ticket(uint32_t *tickets, uint32_t chains)
     return (int)(k + m * atomicAdd(tickets + k * kTicketStride, 1u));
 }
 
+// One lane's 8 running bytes as 4 tagged words, word k at base + 16 k: the 16 lanes of a tile
+// write one contiguous 64-byte segment per store instruction (device-scope stores go past the
+// L2 to memory, where a segment written in part costs as much as a whole one).
 __device__ __forceinline__ void lb_publish(uint32_t *base, uint2 v, uint32_t tag)
 {
     const uint32_t t = tag << 16;
     __hip_atomic_store(base + 0, t | (v.x & 0xffffu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(base + 1, t | (v.x >> 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(base + 2, t | (v.y & 0xffffu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(base + 3, t | (v.y >> 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(base + 16, t | (v.x >> 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(base + 32, t | (v.y & 0xffffu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(base + 48, t | (v.y >> 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// reads one lane's part of a published value; true if all four words carry the tag
+// reads one lane's part of a published value (layout as lb_publish); true if all four words
+// carry the tag
 __device__ __forceinline__ bool lb_read(const uint32_t *base, uint32_t tag, uint2 &v)
 {
     uint32_t w[4];
 #pragma unroll
     for (int k = 0; k < 4; k++)
-        w[k] = __hip_atomic_load(const_cast<uint32_t *>(base) + k, __ATOMIC_RELAXED,
+        w[k] = __hip_atomic_load(const_cast<uint32_t *>(base) + 16 * k, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
     v.x = (w[0] & 0xffffu) | (w[1] << 16);
     v.y = (w[2] & 0xffffu) | (w[3] << 16);
@@ -533,7 +537,7 @@ __device__ __forceinline__ uint2 chain_lookback(uint32_t *lb_agg, uint32_t *lb_i
                                                 uint32_t *err)
 {
     uint2 excl = make_uint2(kOff64, kOff64);
-    const size_t me = (slot * 16 + g) * 4;
+    const size_t me = slot * 64 + g;
     if (tile == 0) {
         lb_publish(lb_incl + me, agg, 2u);
         return excl;
@@ -542,7 +546,7 @@ __device__ __forceinline__ uint2 chain_lookback(uint32_t *lb_agg, uint32_t *lb_i
     size_t pred = slot - step;
     uint32_t spins = 0;
     while (true) {
-        const size_t pw = (pred * 16 + g) * 4;
+        const size_t pw = pred * 64 + g;
         uint2 v;
         if (__ballot(!lb_read(lb_incl + pw, 2u, v)) == 0ull) {
             excl = add_off(excl, v);
