@@ -151,7 +151,11 @@ nq_status nq_encode(const nq_params *p, const void *K, const void *V, const int3
  * values.
  *   K_out, V_out  [L_c][H][n_keep][128] out, fp16 or fp32 per out_dtype
  *   workspace     device scratch of nq_decode_workspace_bytes(p) bytes (tile prefixes of the
- *                 running sum; cleared by the call itself) */
+ *                 running sum; cleared by the call itself, so its contents on entry do not
+ *                 matter; calls sharing one workspace must not overlap). Once the call has
+ *                 completed, the uint32 at word 1 of the workspace is 0; it is nonzero only if
+ *                 a tile's wait for its predecessor's prefix exceeded the kernel's spin limit
+ *                 (2^26 polls, never expected), and the outputs are then invalid. */
 nq_status nq_decode(const nq_params *p, const int8_t *codes_k, const int8_t *codes_v,
                     const void *scales_k, const void *scales_v, const int32_t *positions,
                     const float *rope_cos, const float *rope_sin, void *K_out, void *V_out,
@@ -186,7 +190,8 @@ size_t nq_decode_attend_workspace_bytes(const nq_params *p, int32_t q_heads);
  *   out    fp32 [L_c][q_heads][128] out (zeros when n_keep = 0)
  *   workspace  nq_decode_attend_workspace_bytes(p, q_heads) bytes (look-back words and the
  *              per-tile partials; contents on entry do not matter, calls sharing one
- *              workspace must not overlap) */
+ *              workspace must not overlap; word 1 reports a spin-limit timeout as for
+ *              nq_decode) */
 nq_status nq_decode_attend(const nq_params *p, const int8_t *codes_k, const int8_t *codes_v,
                            const void *scales_k, const void *scales_v, const int32_t *positions,
                            const float *rope_cos, const float *rope_sin, const void *Q,

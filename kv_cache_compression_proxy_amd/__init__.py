@@ -240,6 +240,19 @@ def workspace(nbytes: int, device="cuda"):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def lookback_timed_out(ws) -> bool:
+    """True if the nq_decode / nq_decode_attend call that last used the workspace `ws` gave up
+    a wait for a predecessor tile's prefix (its uint32 word 1, see nq.h; never expected, the
+    outputs are then invalid). Reads the word back, so it waits for that call to finish."""
+    import torch
+    return int(ws[4:8].view(torch.int32).item()) != 0
+
+
+def _check_lookback(fn: str, ws):
+    if lookback_timed_out(ws):
+        raise RuntimeError(f"{fn}: a look-back wait exceeded the spin limit; outputs are invalid")
+
+
 def rope_table(p: NqParams, device="cuda", stream=None):
     import torch
     cos = torch.empty((max(p.tokens, 1), 64), dtype=torch.float32, device=device)
@@ -277,8 +290,9 @@ def compress(K, V, preset: str = "balanced", rope=None, stream=None, window_quer
     return Compressed(p, positions, ck, cv, sk, sv, cos, sin)
 
 
-def decompress(c: Compressed, out_dtype=None, stream=None):
-    """-> (K_hat, V_hat) [Lc, H, n_keep, 128] in fp16 (default) or fp32."""
+def decompress(c: Compressed, out_dtype=None, stream=None, check: bool = False):
+    """-> (K_hat, V_hat) [Lc, H, n_keep, 128] in fp16 (default) or fp32. check: wait for the
+    call and raise if a look-back wait timed out."""
     import torch
     out_dtype = out_dtype or torch.float16
     Lc, H, n, _ = c.codes_k.shape
@@ -288,6 +302,8 @@ def decompress(c: Compressed, out_dtype=None, stream=None):
     nq_decode(c.params, c.codes_k, c.codes_v, c.scales_k, c.scales_v, c.positions, c.rope_cos,
               c.rope_sin, Ko, Vo, NQ_OUT_F32 if out_dtype == torch.float32 else NQ_OUT_F16, ws,
               stream)
+    if check:
+        _check_lookback("nq_decode", ws)
     return Ko, Vo
 
 
@@ -302,18 +318,21 @@ def attend(c_params: NqParams, Q, K_hat, V_hat, stream=None):
     return out
 
 
-def attend_compressed(c: Compressed, Q, stream=None):
+def attend_compressed(c: Compressed, Q, stream=None, check: bool = False):
     """One-token GQA straight from the compressed cache (no K_hat/V_hat written):
-    Q fp16 [Lc, Hq, 128] -> fp32 [Lc, Hq, 128]."""
+    Q fp16 [Lc, Hq, 128] -> fp32 [Lc, Hq, 128]. check: as for decompress."""
     import torch
     Lc, Hq, _ = Q.shape
     out = torch.empty((Lc, Hq, 128), dtype=torch.float32, device=Q.device)
     ws = workspace(nq_decode_attend_workspace_bytes(c.params, Hq), Q.device)
     nq_decode_attend(c.params, c.codes_k, c.codes_v, c.scales_k, c.scales_v, c.positions,
                      c.rope_cos, c.rope_sin, Q, Hq, out, ws, stream)
+    if check:
+        _check_lookback("nq_decode_attend", ws)
     return out
 
 
 __all__ = ["NqParams", "NqError", "Compressed", "PRESETS", "params_for", "make_params",
            "compress", "decompress", "attend", "attend_compressed", "rope_table", "workspace",
+           "lookback_timed_out",
            *EXPORTED]

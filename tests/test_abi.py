@@ -151,3 +151,18 @@ def test_lloyd_max_tables_match_the_oracle():
         assert np.array_equal(t.astype(np.float32), to.astype(np.float32))
     with pytest.raises(nq.NqError):
         nq.nq_lloyd_max_table(5)
+
+
+def test_lookback_flag_reader():
+    """lookback_timed_out reads word 1 of a decode workspace (the spin-limit flag) and nothing
+    else (word 0 holds a ticket counter)."""
+    import torch
+    ws = torch.zeros(256, dtype=torch.uint8)
+    assert not nq.lookback_timed_out(ws)
+    ws[0] = 7
+    assert not nq.lookback_timed_out(ws)
+    ws[4] = 1
+    assert nq.lookback_timed_out(ws)
+    ws[4] = 0
+    ws[7] = 1
+    assert nq.lookback_timed_out(ws)

@@ -72,7 +72,7 @@ def test_fullsize_longctx_and_decode_step():
     out = nq.attend(p, Q, run.K_hat, run.V_hat)
     c = nq.Compressed(p, run.positions, run.codes_k, run.codes_v, run.scales_k, run.scales_v,
                       run.cos, run.sin)
-    fused = nq.attend_compressed(c, Q)
+    fused = nq.attend_compressed(c, Q, check=True)
     torch.cuda.synchronize()
     Ct, St = oracle.rope_table(w.tokens, w.rope_base)
     for lc in (0, w.compressed_layers - 1):
