@@ -672,6 +672,23 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}); "
         f"phases ms: " + ", ".join(f"{k} {v:.3f}" for k, v in phase.items()))
 
+    # the achievable line: torch's device copy of 1 GiB (1 GiB read + 1 GiB written); not in
+    # counter runs, whose copy dispatches calibrate the byte counters
+    copy_gbps = None
+    if not args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(20):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = round(2 * (1 << 30) / (c0.elapsed_time(c1) / 20 * 1e-3) / 1e9, 1)
+        del src, dst
+
     kv_enc = Lc * H * T * 256 * 2
     kv_dec = Lc * H * n_keep * 256 * 2
     value = (kv_enc + kv_dec) / (ms_step * 1e-3) / 1e9
@@ -682,7 +699,9 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": "+".join(PHASE_KERNELS[dom]), "algorithmic_bytes_per_launch": alg[dom],
-                "avg_launch_ms": round(phase[dom], 4)}
+                "avg_launch_ms": round(phase[dom], 4),
+                "traffic_GBps": (None if traffic is None
+                                 else round(traffic / (phase[dom] * 1e-3) / 1e9, 1))}
     out = {
         "metric": "encode/decode fp16-KV GB/s on 1 MI355X; % of HBM peak",
         "value": round(value, 2),
@@ -707,6 +726,7 @@ def main():
             k: round(alg[k] / (phase[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) for k in phase},
         "step_algorithmic_frac_of_peak": round(sum(alg.values()) / (ms_step * 1e-3) / 1e9
                                                / HBM_PEAK_GBPS, 4),
+        "copy_GBps_torch": copy_gbps,
         "roofline": roofline,
         "cpu_baseline": None,
     }
