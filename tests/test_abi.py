@@ -166,3 +166,27 @@ def test_lookback_flag_reader():
     ws[4] = 0
     ws[7] = 1
     assert nq.lookback_timed_out(ws)
+
+
+@pytest.mark.parametrize("case", ["no-tokens", "no-compressed-layers"])
+def test_empty_caches_return_before_any_launch(case):
+    """An empty cache (T = 0) or an empty compressed range (layer_begin == layer_end) makes every
+    entry point return NQ_OK before touching the device or its pointers (here all NULL); the
+    fused decode-attention still writes its zero output when there are layers but no tokens,
+    so it is exercised only on the empty range."""
+    T, end = (0, 2) if case == "no-tokens" else (64, 0)
+    p = nq.make_params(2, 2, T, 16, 600, 3, 2, 1e4, 0, end)
+    assert nq.nq_check_params(p) == nq.NQ_OK
+    L, P = nq._lib, C.byref(p)
+    n = None
+    assert L.nq_score_evict(P, n, n, n, n, 0, n) == nq.NQ_OK
+    assert L.nq_score_evict_attn(P, n, n, 4, n, n, n, 0, n) == nq.NQ_OK
+    assert L.nq_encode(P, n, n, n, n, n, n, n, n, n, n) == nq.NQ_OK
+    assert L.nq_decode(P, n, n, n, n, n, n, n, n, n, nq.NQ_OUT_F16, n, 0, n) == nq.NQ_OK
+    assert L.nq_encode_scalar(P, n, n, n, n, n, n, n, n, n, n) == nq.NQ_OK
+    assert L.nq_decode_scalar(P, n, n, n, n, n, n, n, n, n, nq.NQ_OUT_F16, n) == nq.NQ_OK
+    if case == "no-tokens":
+        assert L.nq_rope_table(P, n, n, n) == nq.NQ_OK
+    else:
+        assert L.nq_attend_decode(P, n, 4, n, n, 10, n, n, 0, n) == nq.NQ_OK
+        assert L.nq_decode_attend(P, n, n, n, n, n, n, n, n, 4, n, n, 0, n) == nq.NQ_OK
