@@ -73,6 +73,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PHASE_KERNELS = {"score_evict": ("k_window_sum", "k_scores", "k_select", "k_select_reg"),
                  "encode": ("k_encode",),
                  "decode": ("k_decode_reset", "k_decode")}
+# the fused decode step's kernels (bench.py --decode-step)
+DECODE_STEP_KERNELS = {"decode_attend": ("k_decode_reset", "k_decode_attend",
+                                         "k_decode_attend_merge")}
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -89,13 +92,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_path(w) -> str:
-    return os.path.join(ROOT, "profiles", f"hbm_traffic_{w.name}.md")
+def traffic_path(w, decode_step: bool = False) -> str:
+    name = f"decode-step_{w.name}" if decode_step else w.name
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{name}.md")
 
 
-def summarize_pmc(args, w):
-    """rocprofv3 counter CSVs -> profiles/hbm_traffic_<workload>.md. FETCH_SIZE and WRITE_SIZE
-    (KiB per dispatch) are scaled by what they read for a device copy of known size."""
+def summarize_pmc(args, w, decode_step: bool = False):
+    """rocprofv3 counter CSVs -> profiles/hbm_traffic_<workload>.md (the headline step's phases)
+    or profiles/hbm_traffic_decode-step_<cache>.md (the fused decode step, --decode-step).
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read for a device copy
+    of known size."""
     import csv
     from collections import defaultdict
 
@@ -107,7 +113,12 @@ def summarize_pmc(args, w):
                 name = r["Kernel_Name"].split("(")[0].split("<")[0]
                 name = name.replace("void ", "").replace("nq::", "").strip()
                 vals[name].append(float(r["Counter_Value"]))
-        return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+        out = {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+        # the runtime's copy kernel also stages the host-to-device input uploads (smaller
+        # copies): the calibration copy is its largest dispatch
+        if COPY_KERNEL in vals:
+            out[COPY_KERNEL] = (max(vals[COPY_KERNEL]), len(vals[COPY_KERNEL]))
+        return out
 
     fetch = per_kernel(args.summarize_pmc[0], "FETCH_SIZE")
     write = per_kernel(args.summarize_pmc[1], "WRITE_SIZE")
@@ -116,7 +127,8 @@ def summarize_pmc(args, w):
         sys.exit("--summarize-pmc needs the runs' --copy-calibration size and its copy kernel")
     fk = copy_bytes / (fetch[COPY_KERNEL][0] * 1024)
     wk = copy_bytes / (write[COPY_KERNEL][0] * 1024)
-    lines = [f"# HBM traffic per launch: {w.name}", "",
+    title = f"fused decode step over {w.name}" if decode_step else w.name
+    lines = [f"# HBM traffic per launch: {title}", "",
              "rocprofv3 counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the "
              "run's dispatches), each in a run of its own, scaled by what the same counter reads "
              f"for a plain device copy of {args.copy_calibration} MiB ({COPY_KERNEL}: reads and "
@@ -137,12 +149,12 @@ def summarize_pmc(args, w):
                      f"{wr * 1024 * wk / 1e9:.4f} |")
     lines += ["", "Per launch of each phase (bytes; the figures bench.py reports as `traffic`):",
               "", "```"]
-    for ph, ks in PHASE_KERNELS.items():
+    for ph, ks in (DECODE_STEP_KERNELS if decode_step else PHASE_KERNELS).items():
         tot = sum(fetch.get(k, (0.0, 0))[0] * 1024 * fk + write.get(k, (0.0, 0))[0] * 1024 * wk
                   for k in ks)
         lines.append(f"traffic {ph} {int(round(tot))}")
     lines += [f"kernel-sources {kernel_source_hash()}", "```", ""]
-    out = traffic_path(w)
+    out = traffic_path(w, decode_step)
     open(out, "w").write("\n".join(lines))
     log(f"[bench] wrote {out}")
 
@@ -503,6 +515,13 @@ def decode_step(args):
     del K, V
     torch.cuda.empty_cache()
     log(f"[decode-step] compressed cache built in {time.time() - t0:.1f}s")
+    if args.copy_calibration:   # the copy whose counters calibrate a --pmc run
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     Hq = w4.q_heads
     Q = torch.from_numpy(kvsynth.queries(w4)).to(dev)
     out = torch.empty((Lc, Hq, 128), dtype=torch.float32, device=dev)
@@ -570,8 +589,10 @@ def decode_step(args):
         "two_call_value": round(kv16 / (ms_2 * 1e-3) / 1e9, 2),
         "max_abs_diff_vs_two_call_rel": float(f"{diff:.3e}"),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "k_decode_reset+k_decode_attend+k_decode_attend_merge",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": read_traffic(args.traffic or traffic_path(w, decode_step=True),
+                                             "decode_attend"),
+                     "kernel": "+".join(DECODE_STEP_KERNELS["decode_attend"]),
                      "algorithmic_bytes_per_launch": alg_f, "avg_launch_ms": round(ms_f, 4)},
         "two_call_algorithmic_frac_of_peak": round(alg_2 / (ms_2 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                                    4),
@@ -589,7 +610,10 @@ def main():
     import kvsynth
     w = kvsynth.workload(args.workload)
     if args.summarize_pmc:
-        summarize_pmc(args, w)
+        if args.decode_step:
+            summarize_pmc(args, kvsynth.workload(2), decode_step=True)
+        else:
+            summarize_pmc(args, w)
         return
     if args.decode_step:
         decode_step(args)

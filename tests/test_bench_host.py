@@ -51,7 +51,7 @@ def test_traffic_summary_round_trip(tmp_path, monkeypatch):
     the source hash and read back; a different hash reads as absent."""
     w = kvsynth.workload(1)
     out = tmp_path / "traffic.md"
-    monkeypatch.setattr(bench, "traffic_path", lambda _w: str(out))
+    monkeypatch.setattr(bench, "traffic_path", lambda _w, decode_step=False: str(out))
     copy = bench.COPY_KERNEL
     # the copy of 1 MiB reads 512 KiB by FETCH_SIZE (factor 2) and 1024 KiB by WRITE_SIZE
     _counter_csv(tmp_path / "f", [(copy, "FETCH_SIZE", 512),
@@ -81,3 +81,32 @@ def test_traffic_summary_round_trip(tmp_path, monkeypatch):
     out.write_text(txt)
     assert bench.read_traffic(str(out), "encode") is None
     assert bench.read_traffic(str(tmp_path / "missing.md"), "encode") is None
+
+
+def test_decode_step_traffic_and_copy_calibration(tmp_path, monkeypatch):
+    """The fused decode step's summary sums its own kernels; the calibration uses the largest
+    copy dispatch (the runtime's copy kernel also stages smaller input uploads)."""
+    w = kvsynth.workload(2)
+    out = tmp_path / "ds.md"
+    seen = []
+    monkeypatch.setattr(bench, "traffic_path",
+                        lambda _w, decode_step=False: seen.append(decode_step) or str(out))
+    copy = bench.COPY_KERNEL
+    _counter_csv(tmp_path / "f", [(copy, "FETCH_SIZE", 3), (copy, "FETCH_SIZE", 512),
+                                  ("void nq::k_decode_attend<4>(nq::FusedArgs)", "FETCH_SIZE", 80),
+                                  ("void nq::k_decode_attend_merge<4>(nq::FusedArgs)",
+                                   "FETCH_SIZE", 4),
+                                  ("nq::k_decode(nq::CodecArgs)", "FETCH_SIZE", 999)])
+    _counter_csv(tmp_path / "w", [(copy, "WRITE_SIZE", 1), (copy, "WRITE_SIZE", 1024),
+                                  ("void nq::k_decode_attend<4>(nq::FusedArgs)", "WRITE_SIZE", 6),
+                                  ("nq::k_decode_reset(unsigned int*, long, unsigned int*)",
+                                   "WRITE_SIZE", 2)])
+
+    class A:
+        summarize_pmc = (str(tmp_path / "f"), str(tmp_path / "w"))
+        copy_calibration = 1
+        pmc_command = "(test)"
+    bench.summarize_pmc(A, w, decode_step=True)
+    assert seen == [True]
+    assert bench.read_traffic(str(out), "decode_attend") == ((80 + 4) * 2 + 6 + 2) * 1024
+    assert bench.read_traffic(str(out), "encode") is None
