@@ -69,6 +69,11 @@ def test_group_quantization_known_answers():
     assert np.array_equal(i_got, idx)
     z16, z_idx, _ = quantize_group(np.zeros(8, np.float32), 2)
     assert z16 == 0 and np.all(z_idx == 2)
+    # a coordinate exactly on a threshold takes the lower cell: u = 0 sits on the middle
+    # threshold, which is exactly 0 (the tables are antisymmetric)
+    for bits in (2, 3, 4):
+        _, on_idx, _ = quantize_group(np.array([0, 1, -1, 1, -1, 1, -1, 1], np.float32), bits)
+        assert on_idx[0] == (1 << (bits - 1)) - 1
     # an RMS beyond the fp16 range keeps the largest finite scale; u then lies beyond every
     # threshold in magnitude, so the indices are the outermost cells
     big = np.array([2e5, -2e5, 2e5, -2e5, 2e5, -2e5, 2e5, -2e5], np.float32)
@@ -84,6 +89,10 @@ def test_decode_inverts_the_rotation():
     sc = np.full((1, 1, 16), oracle.f2h_rne(0.5), np.uint16)
     y32, _ = tables_f32(3)
     Ct, St = oracle.rope_table(4, 1e4)
-    _, Vh = decode_layer(idx, idx, sc, sc, np.array([2]), Ct, St, 3, 3)
+    Kh, Vh = decode_layer(idx, idx, sc, sc, np.array([2]), Ct, St, 3, 3)
     ref = oracle.fwht_f64(0.5 * y32.astype(np.float64)[idx[0, 0]])
     assert np.max(np.abs(Vh[0, 0] - ref)) < 1e-15
+    # keys get the rotary embedding of their position back: removing it with the pinned
+    # RoPE removal of the codec (fp32) returns the rotated-back row
+    back = oracle.rope_undo(Kh[0, 0].astype(np.float32), Ct[2], St[2]).astype(np.float64)
+    assert np.max(np.abs(back - ref)) < 1e-6 * np.max(np.abs(ref))

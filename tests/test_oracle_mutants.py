@@ -1,14 +1,19 @@
 """The oracle's pins have teeth. Each plausible mistake below is planted in a copy of the
-oracle's C source: a flipped sign, a dropped term, a wrong index or bound, a swapped operand, or
-a wrong rounding or tie rule. The copy is built with the oracle's own flags, and the pin tests
-it concerns run against it in a subprocess (NQ_ORACLE_LIB points the wrapper at the mutant).
-Every mutant must make them fail. The unmodified source, built the same way, must pass them.
+oracle's source: a flipped sign, a dropped term, a wrong index or bound, a swapped operand, or a
+wrong rounding or tie rule. The pin tests it concerns then run against the copy in a subprocess,
+and every mutant must make them fail. The unmodified source, run the same way, must pass them.
+- C oracle: the copy is built with the oracle's own flags, and NQ_ORACLE_LIB points the wrapper
+  at it.
+- numpy oracles (the attention-weight scorer, the Lloyd-Max baseline): the pins run from a copy
+  of the tests and oracle packages with the mutated module.
 Nothing here touches a GPU or the GPU library's arithmetic.
 """
 import os
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
+
+import shutil
 
 import pytest
 
@@ -106,5 +111,80 @@ def test_every_planted_mistake_fails_a_pin(tmp_path):
     with ThreadPoolExecutor(4) as ex:
         results = list(ex.map(one, range(len(MUTANTS))))
     # 1: a pin failed; negative: the mutant crashed the test process (also caught)
+    survivors = [name for name, rc in results if not (rc == 1 or rc < 0)]
+    assert not survivors, f"mistakes no pin catches: {survivors}"
+
+
+ATT = "tests/test_oracle_attn_scorer.py"
+LM = "tests/test_oracle_lloyd_max.py"
+
+# (what the mistake is, module file, exact text, replacement, pin file that must catch it)
+PY_MUTANTS = [
+    ("attention scorer: logits scaled by 1/128", "attn_scorer.py",
+     "/ np.sqrt(float(D))", "/ float(D)", ATT),
+    ("attention scorer: query head j reads kv head j mod H", "attn_scorer.py",
+     "K[j // G].T", "K[j % H].T", ATT),
+    ("attention scorer: a query does not see its own position", "attn_scorer.py",
+     "z = Z[w, :P + 1]", "z = Z[w, :P]", ATT),
+    ("attention scorer: window positions shifted by one", "attn_scorer.py",
+     "P = T - W + w ", "P = T - W + w - 1 ", ATT),
+    ("Lloyd-Max: centroid with the wrong sign", "lloyd_max.py",
+     "y_new = np.array([(_phi(a) - _phi(b))", "y_new = np.array([(_phi(b) - _phi(a))", LM),
+    ("Lloyd-Max: thresholds not at the midpoints", "lloyd_max.py",
+     "        t = 0.5 * (y[:-1] + y[1:])\n", "        t = 0.45 * (y[:-1] + y[1:])\n", LM),
+    ("Lloyd-Max: RMS over 4 instead of 8 values", "lloyd_max.py",
+     "ss * np.float32(0.125)", "ss * np.float32(0.25)", LM),
+    ("Lloyd-Max: a value on a threshold takes the upper cell", "lloyd_max.py",
+     "int(np.sum(t32 < ui))", "int(np.sum(t32 <= ui))", LM),
+    ("Lloyd-Max: all-zero group indexed 0", "lloyd_max.py",
+     "np.full(8, 1 << (bits - 1), np.uint8)", "np.zeros(8, np.uint8)", LM),
+    ("Lloyd-Max: scale not saturated at 65504", "lloyd_max.py",
+     "s16 = min(f2h_rne(float(s32)), 0x7BFF)", "s16 = f2h_rne(float(s32))", LM),
+    ("Lloyd-Max: decode without the 1/sqrt(128)", "lloyd_max.py",
+     "        x = x / math.sqrt(128.0)\n", "", LM),
+    ("Lloyd-Max: decode restores RoPE with the wrong sign", "lloyd_max.py",
+     "x[..., 64:] = hi * C + lo * S", "x[..., 64:] = hi * C - lo * S", LM),
+]
+
+
+def _py_pins(root: str, test_file: str) -> int:
+    env = dict(os.environ, NQ_ORACLE_LIB=oracle_build.LIB)
+    r = subprocess.run([sys.executable, "-m", "pytest", test_file, "-x", "-q", "-m", "not gpu",
+                        "-p", "no:cacheprovider"], cwd=root, env=env, capture_output=True,
+                       text=True, timeout=600)
+    return r.returncode
+
+
+def _tree(dst: str) -> None:
+    """A copy of what the numpy oracles' pins import: tests, oracle (sources only), kvsynth."""
+    ign = shutil.ignore_patterns("_build", "__pycache__", "*.so")
+    for d in ("tests", "oracle", "kvsynth"):
+        shutil.copytree(os.path.join(ROOT, d), os.path.join(dst, d), ignore=ign)
+    shutil.copy(os.path.join(ROOT, "pytest.ini"), dst)
+
+
+def test_every_planted_mistake_in_the_numpy_oracles_fails_a_pin(tmp_path):
+    if not os.path.exists(oracle_build.LIB):
+        oracle_build.build()
+    srcs = {}
+    for name, mod, old, new, _ in PY_MUTANTS:
+        if mod not in srcs:
+            srcs[mod] = open(os.path.join(ROOT, "oracle", mod)).read()
+        assert srcs[mod].count(old) == 1, f"mutation site not unique or missing: {name}"
+    clean = str(tmp_path / "clean")
+    _tree(clean)
+    assert _py_pins(clean, ATT) == 0 and _py_pins(clean, LM) == 0, \
+        "the pins fail on the unmodified numpy oracles"
+
+    def one(k):
+        name, mod, old, new, pin = PY_MUTANTS[k]
+        root = str(tmp_path / f"mutant{k}")
+        _tree(root)
+        with open(os.path.join(root, "oracle", mod), "w") as f:
+            f.write(srcs[mod].replace(old, new))
+        return name, _py_pins(root, pin)
+
+    with ThreadPoolExecutor(4) as ex:
+        results = list(ex.map(one, range(len(PY_MUTANTS))))
     survivors = [name for name, rc in results if not (rc == 1 or rc < 0)]
     assert not survivors, f"mistakes no pin catches: {survivors}"
