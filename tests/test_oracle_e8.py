@@ -109,3 +109,18 @@ def test_normalized_second_moment():
     assert abs(G - GOLD["normalized_second_moment"]["value"]) < 4e-4
     # a Z^8 quantizer would give 1/12; D8-only decoding also lands well above E8's value
     assert G < 0.074
+
+
+def test_exact_tie_rules():
+    """The oracle's rules on exact ties (measure zero; the readings of the nearest-point step):
+    the integer coset wins a distance tie, rint rounds ties to even, and a coordinate with zero
+    error moves toward zero when the parity fix falls on it."""
+    cases = [
+        ([0.25] * 8, [0] * 8),                     # both cosets at squared distance 1/2
+        ([2.5, 0.5, 0, 0, 0, 0, 0, 0], [4, 0, 0, 0, 0, 0, 0, 0]),   # ties to even: (2, 0, ...)
+        ([1, 0, 0, 0, 0, 0, 0, 0], [0] * 8),       # odd sum, all errors 0: index 0 moves to 0
+        ([-1, 0, 0, 0, 0, 0, 0, 0], [0] * 8),
+    ]
+    for u, want in cases:
+        c, _ = oracle.e8_nearest(np.array([u], np.float32))
+        assert list(c[0]) == want, (u, list(c[0]))

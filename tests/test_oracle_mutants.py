@@ -75,6 +75,55 @@ MUTANTS = [
      "double scale = 1.0 / sqrt(128.0);", "double scale = 1.0;", [PATH]),
     ("attention: query head j reads kv head j mod H",
      "int32_t h = j / grp;", "int32_t h = j % H;", [PATH]),
+    ("group scale: no clamp at +rho", "if (q > rho) q = rho;", "", [PATH]),
+    ("group scale: no clamp at -rho", "if (q < -rho) q = -rho;", "", [PATH]),
+    ("group scale: the absmax skips the first coordinate",
+     "for (int i = 0; i < 8; i++) a = fabsf(xg[i]) > a ? fabsf(xg[i]) : a;",
+     "for (int i = 1; i < 8; i++) a = fabsf(xg[i]) > a ? fabsf(xg[i]) : a;", [PATH]),
+    ("selection: the window starts one token late",
+     "keep[t] = (t == 0 || t >= c_end) ? 1 : 0;", "keep[t] = (t == 0 || t > c_end) ? 1 : 0;",
+     [PATH]),
+    ("selection: BOS not protected",
+     "keep[t] = (t == 0 || t >= c_end) ? 1 : 0;", "keep[t] = (t >= c_end) ? 1 : 0;", [PATH]),
+    ("selection: one candidate too many",
+     "for (int32_t i = 0; i < m; i++) keep[c[i].t] = 1;",
+     "for (int32_t i = 0; i <= m && i < n_cand; i++) keep[c[i].t] = 1;", [PATH]),
+    ("keep count: BOS not counted among the protected",
+     "int64_t prot = (int64_t)W + 1 < T ? (int64_t)W + 1 : T;",
+     "int64_t prot = (int64_t)W < T ? (int64_t)W : T;", [PATH]),
+    ("rotary table: angles in fp32",
+     "double phi = (double)p * theta[i];", "double phi = (double)((float)p * (float)theta[i]);",
+     [NUM]),
+    ("fp16 round-up: rounds to nearest",
+     "uint16_t nqo_f2h_ceil(float v)\n{", "uint16_t nqo_f2h_ceil(float v)\n{\n    return nqo_f2h_rne(v);",
+     [NUM]),
+    ("fp16 to fp32: subnormals flushed to zero",
+     "float nqo_h2f(uint16_t h)\n{",
+     "float nqo_h2f(uint16_t h)\n{\n    if (((h >> 10) & 0x1f) == 0) return (h & 0x8000) ? -0.0f : 0.0f;",
+     [NUM]),
+    ("E8: a distance tie goes to the half-integer coset",
+     "const double *y = (d0 <= d1) ? y0 : y1;", "const double *y = (d0 < d1) ? y0 : y1;", [E8]),
+    ("E8: rint ties away from zero",
+     "f[i] = nearbyint(v[i]); sum += f[i];", "f[i] = round(v[i]); sum += f[i];", [E8]),
+    ("E8: a zero-error coordinate moves away from zero",
+     "else f[j] += (f[j] > 0.0) ? -1.0 : 1.0;", "else f[j] += (f[j] > 0.0) ? 1.0 : -1.0;", [E8]),
+    ("decode: the running sum not taken mod 256",
+     "c[i] = (int)(int8_t)(uint8_t)((c[i] + d[o * HD + i]) & 0xff);",
+     "c[i] = c[i] + d[o * HD + i];", [PATH]),
+    ("decode: the scale of the wrong group",
+     "double s = (double)nqo_h2f(scales[o * NG + i / 8]);",
+     "double s = (double)nqo_h2f(scales[o * NG + i % 16]);", [PATH]),
+    ("attention: softmax without the maximum subtracted",
+     "for (int32_t t = 0; t < n; t++) { z[t] = exp(z[t] - mx); den += z[t]; }",
+     "for (int32_t t = 0; t < n; t++) { z[t] = exp(z[t]); den += z[t]; }", [PATH]),
+    ("nominal ratio: one scale per group instead of two",
+     "2.0 * 16.0 * 16.0", "16.0 * 16.0", [PATH]),
+    ("encode: keys not rotated back",
+     "            if (is_key)\n                nqo_rope_undo(", "            if (0)\n                nqo_rope_undo(",
+     [PATH]),
+    ("encode: values rotated back too",
+     "            if (is_key)\n                nqo_rope_undo(", "            if (1)\n                nqo_rope_undo(",
+     [PATH]),
 ]
 
 

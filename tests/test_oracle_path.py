@@ -63,6 +63,10 @@ def test_quantize_row_scale_rule_and_composition(bits):
         x = (rng.standard_normal(128) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
         if trial == 0:
             x[:8] = 0                                      # an all-zero group
+            # groups whose a/rho exceeds the fp16 range: the scale saturates at 65504 and the
+            # clamp to [-rho, rho] decides the point
+            x[8:16] = [1e6, 0, 3, 0, 0, 0, 0, 0]
+            x[16:24] = [-1e6, 0, 0, -5, 0, 0, 0, 0]
         s16, c, fl = oracle.quantize_row(x, bits)
         for g in range(16):
             xg = x[8 * g:8 * g + 8]
@@ -73,7 +77,10 @@ def test_quantize_row_scale_rule_and_composition(bits):
             v = np.float32(a / np.float32(rho))             # IEEE fp32 division (numpy)
             s = np.uint16(s16[g]).view(np.float16).astype(np.float32)
             below = np.uint16(s16[g] - 1).view(np.float16).astype(np.float32)
-            assert s >= v and below < v                    # smallest binary16 >= a/rho
+            if v > 65504:
+                assert s16[g] == 0x7BFF                    # saturated
+            else:
+                assert s >= v and below < v                # smallest binary16 >= a/rho
             u = np.clip(xg / s, -rho, rho).astype(np.float32)
             assert np.max(np.abs(u)) <= rho
             cref, _ = oracle.e8_nearest(u[None])
@@ -126,6 +133,21 @@ def test_constant_values_give_zero_deltas_and_roundtrip():
             x = oracle.fwht_f32(oracle.rope_undo(K[h, p].astype(np.float32), Ct[p], St[p]))
             _, c, _ = oracle.quantize_row(x, 3)
             assert np.array_equal(absk[h, j], c)
+
+
+def test_running_sum_wraps_mod_256():
+    """Decode's running sum is taken mod 256 as int8, whatever the byte stream: deltas of 100
+    give the codes 100, -56, 44, -112 (values decode to H(s*c/2), and H is its own inverse)."""
+    H, n = 1, 4
+    d = np.full((H, n, 128), 100, np.int8)
+    sc = np.full((H, n, 16), oracle.f2h_rne(1.0), np.uint16)
+    Ct, St = oracle.rope_table(4, 1e4)
+    pos = np.arange(n, dtype=np.int32)
+    _, Vh = oracle.decode_layer(d, d, sc, sc, pos, Ct, St)
+    want = ((np.cumsum(d.astype(np.int64), axis=1) + 128) % 256 - 128).astype(np.float64)
+    assert list(want[0, :, 0]) == [100, -56, 44, -112]
+    for j in range(n):
+        assert np.allclose(2.0 * oracle.fwht_f64(Vh[0, j]), want[0, j], atol=1e-9)
 
 
 def test_lattice_exact_rows_roundtrip():
@@ -192,6 +214,14 @@ def test_attend_special_cases():
     assert np.allclose(out, V[0].mean(0)[None], atol=1e-14)
     one = oracle.attend_layer(np.ones((4, 128), np.float16), np.ones((1, 1, 128)), V[:, :1])
     assert np.allclose(one, V[0, 0][None], atol=0)
+    # logits far beyond exp's range: with the maximum subtracted the weights are one-hot on the
+    # largest logit (the textbook softmax, not inf / inf)
+    qb = np.zeros((1, 128), np.float16)
+    qb[0, 0] = 60000
+    Kb = np.zeros((1, 3, 128))
+    Kb[0, :, 0] = [0.0, 1000.0, 2000.0]
+    big = oracle.attend_layer(qb, Kb, V[:, :3])
+    assert np.all(np.isfinite(big)) and np.allclose(big[0], V[0, 2], atol=0)
 
 
 # ---------------------------------------------------------------- nominal ratio
