@@ -53,6 +53,9 @@ def lib():
             "nqo_e8_nearest_many": (None, [_f32, C.c_int64, _i8, _f64]),
             "nqo_e8_margin": (C.c_double, [_f32, _i8]),
             "nqo_quantize_row": (None, [_f32, C.c_int32, _u16, _i8, _u8]),
+            "nqo_group_u": (C.c_float, [_f32, C.c_uint16, C.c_int32, _f32]),
+            "nqo_voronoi_near_tie": (C.c_int, [_f32, _i8, C.c_float]),
+            "nqo_scale_near_tie": (C.c_int, [C.c_float, C.c_uint16]),
             "nqo_encode_layer": (None, [_u16, _u16, C.c_int32, C.c_int32, _i32, C.c_int32, _f32,
                                         _f32, C.c_int32, C.c_int32, _i8, _i8, _u16, _u16, _u8,
                                         _u8]),
@@ -144,6 +147,34 @@ def quantize_row(x: np.ndarray, bits: int):
     f = np.empty(16, np.uint8)
     lib().nqo_quantize_row(np.ascontiguousarray(x, np.float32), bits, s, c, f)
     return s, c, f
+
+
+def group_u(xg: np.ndarray, s16: int, bits: int):
+    """The lattice-step input of one rotated 8-float group at the fp16 scale bits s16:
+    -> (u float32 [8], max |u|)."""
+    u = np.empty(8, np.float32)
+    m = lib().nqo_group_u(np.ascontiguousarray(xg, np.float32), int(s16), bits, u)
+    return u, m
+
+
+def voronoi_near_tie(u: np.ndarray, c: np.ndarray) -> bool:
+    u = np.ascontiguousarray(u, np.float32)
+    return bool(lib().nqo_voronoi_near_tie(u, np.ascontiguousarray(c, np.int8),
+                                           float(np.abs(u).max())))
+
+
+def scale_near_tie(v: float, s16: int) -> bool:
+    """v = fp32(a / rho), s16 = its rounded-up fp16 scale bits."""
+    return bool(lib().nqo_scale_near_tie(float(np.float32(v)), int(s16)))
+
+
+def rotated_row(row16: np.ndarray, is_key: bool, Crow=None, Srow=None) -> np.ndarray:
+    """The codec's front end for one stored fp16 row: RoPE removal (keys, at the row's
+    position) then the normalised Hadamard rotation -> float32 [128]."""
+    k = np.asarray(row16).view(np.float16).astype(np.float32) if np.asarray(row16).dtype == np.uint16 \
+        else np.asarray(row16, np.float16).astype(np.float32)
+    x = rope_undo(k, Crow, Srow) if is_key else k
+    return fwht_f32(x)
 
 
 # --- per-layer path --------------------------------------------------------------------------

@@ -105,11 +105,20 @@ def quantize_group(x8: np.ndarray, bits: int):
             near |= abs(float(s32) - b) <= 1e-6 * float(s32)
     if s == 0:
         return s16, np.full(8, 1 << (bits - 1), np.uint8), near
-    u = (x8.astype(np.float32) / s).astype(np.float32)
-    idx = np.array([int(np.sum(t32 < ui)) for ui in u], np.uint8)
+    idx, u = indices_at(x8, s16, bits)
     for ui in u:
         near |= bool(np.any(np.abs(ui - t32) <= 1e-6 * np.maximum(1.0, np.abs(t32))))
     return s16, idx, near
+
+
+def indices_at(x8: np.ndarray, s16: int, bits: int):
+    """The quantizer step of one group at the fp16 scale bits s16 (nonzero): u = x / s in fp32,
+    index = number of fp32 thresholds strictly below u. -> (indices uint8 [8], u float32 [8])."""
+    _, t32 = tables_f32(bits)
+    s = np.float32(h2f(int(s16)))
+    u = (x8.astype(np.float32) / s).astype(np.float32)
+    idx = np.array([int(np.sum(t32 < ui)) for ui in u], np.uint8)
+    return idx, u
 
 
 def encode_layer(K_l, V_l, positions, Ctab, Stab, bits_k: int, bits_v: int):

@@ -316,9 +316,48 @@ void nqo_e8_nearest_many(const float *u, int64_t n_groups, int8_t *c, double *ma
  * ---------------------------------------------------------------------------------------- */
 static float h2f_next_down(uint16_t h) { return h == 0 ? 0.0f : nqo_h2f((uint16_t)(h - 1)); }
 
+/* the radius rho_b = 2^(b-1) - 1 of a b-bit budget */
+static float radius(int32_t bits) { return (float)((1 << (bits - 1)) - 1); }
+
+/* the lattice-step input of one group at the fp16 scale s16: u_i = x_i / s (fp32, correctly
+ * rounded), clamped to [-rho, rho] (the clamp only acts when the scale saturated); returns
+ * max |u_i| */
+float nqo_group_u(const float *xg, uint16_t s16, int32_t bits, float *u)
+{
+    float rho = radius(bits);
+    float s = nqo_h2f(s16), umax = 0.0f;
+    for (int i = 0; i < 8; i++) {
+        float q = s16 ? xg[i] / s : 0.0f;
+        if (q > rho) q = rho;
+        if (q < -rho) q = -rho;
+        u[i] = q;
+        if (fabsf(q) > umax) umax = fabsf(q);
+    }
+    return umax;
+}
+
+/* Voronoi near-tie: the facet distance of u - c/2 below 1e-6 * max(1, |u|_inf) */
+int nqo_voronoi_near_tie(const float *u, const int8_t *c, float umax)
+{
+    double lim = 1e-6 * (umax > 1.0f ? (double)umax : 1.0);
+    return nqo_e8_margin(u, c) < lim;
+}
+
+/* Scale near-tie: v = fp32(a / rho) within 1e-6 relative of a binary16 value at which the
+ * rounded-up scale changes: the scale h itself (v a little larger would give the next fp16)
+ * or the fp16 value below it (v a little smaller would give that one). A saturated scale has
+ * no upper step: every larger v keeps 65504. */
+int nqo_scale_near_tie(float v, uint16_t h)
+{
+    double dv = (double)v, lo = (double)h2f_next_down(h), hi = (double)nqo_h2f(h);
+    int near_lo = dv - lo <= 1e-6 * dv;
+    int near_hi = h != 0x7bff && hi - dv <= 1e-6 * dv;
+    return near_lo || near_hi;
+}
+
 void nqo_quantize_row(const float *x, int32_t bits, uint16_t *s16, int8_t *c, uint8_t *flags)
 {
-    float rho = (float)((1 << (bits - 1)) - 1);
+    float rho = radius(bits);
     for (int g = 0; g < NG; g++) {
         const float *xg = x + 8 * g;
         float a = 0.0f;
@@ -330,24 +369,12 @@ void nqo_quantize_row(const float *x, int32_t bits, uint16_t *s16, int8_t *c, ui
         } else {
             float v = a / rho;
             uint16_t h = nqo_f2h_ceil(v);
-            float s = nqo_h2f(h);
-            float u[8], umax = 0.0f;
-            for (int i = 0; i < 8; i++) {
-                float q = xg[i] / s;
-                if (q > rho) q = rho;
-                if (q < -rho) q = -rho;
-                u[i] = q;
-                if (fabsf(q) > umax) umax = fabsf(q);
-            }
+            float u[8];
+            float umax = nqo_group_u(xg, h, bits, u);
             s16[g] = h;
             nqo_e8_nearest(u, c + 8 * g);
-            double lim = 1e-6 * (umax > 1.0f ? (double)umax : 1.0);
-            if (nqo_e8_margin(u, c + 8 * g) < lim) fl |= 1;
-            if (h != 0x7bff) {
-                double lo = (double)h2f_next_down(h), hi = (double)s;
-                double dv = (double)v;
-                if (dv - lo <= 1e-6 * dv || hi - dv <= 1e-6 * dv) fl |= 2;
-            }
+            if (nqo_voronoi_near_tie(u, c + 8 * g, umax)) fl |= 1;
+            if (nqo_scale_near_tie(v, h)) fl |= 2;
         }
         if (flags) flags[g] = fl;
     }

@@ -24,6 +24,7 @@ from oracle import build as oracle_build  # noqa: E402
 NUM = "tests/test_oracle_numeric.py"
 E8 = "tests/test_oracle_e8.py"
 PATH = "tests/test_oracle_path.py"
+NT = "tests/test_oracle_near_ties.py"
 
 # (what the mistake is, exact text in nq_oracle.c, replacement, pin files that must catch it)
 MUTANTS = [
@@ -62,7 +63,7 @@ MUTANTS = [
     ("group scale: rounded to nearest instead of up",
      "uint16_t h = nqo_f2h_ceil(v);", "uint16_t h = nqo_f2h_rne(v);", [PATH]),
     ("group scale: radius 2^b - 1 instead of 2^(b-1) - 1",
-     "float rho = (float)((1 << (bits - 1)) - 1);", "float rho = (float)((1 << bits) - 1);",
+     "return (float)((1 << (bits - 1)) - 1);", "return (float)((1 << bits) - 1);",
      [PATH]),
     ("delta coding: previous minus current",
      "cur[i] = (int8_t)(uint8_t)(((int)cur[i] - (int)prev[i]) & 0xff);",
@@ -124,6 +125,37 @@ MUTANTS = [
     ("encode: values rotated back too",
      "            if (is_key)\n                nqo_rope_undo(", "            if (1)\n                nqo_rope_undo(",
      [PATH]),
+    # the near-tie classification: it decides which GPU results may differ from the oracle's
+    ("Voronoi near-tie: every group flagged",
+     "return nqo_e8_margin(u, c) < lim;", "return 1;", [NT]),
+    ("Voronoi near-tie: no group flagged",
+     "return nqo_e8_margin(u, c) < lim;", "return 0;", [NT]),
+    ("Voronoi near-tie: band 1000x too wide",
+     "double lim = 1e-6 * (umax", "double lim = 1e-3 * (umax", [NT]),
+    ("Voronoi near-tie: band not scaled by the largest coordinate",
+     "double lim = 1e-6 * (umax > 1.0f ? (double)umax : 1.0);", "double lim = 1e-6;", [NT]),
+    ("scale near-tie: every group flagged",
+     "return near_lo || near_hi;", "return 1;", [NT]),
+    ("scale near-tie: no group flagged",
+     "return near_lo || near_hi;", "return 0;", [NT]),
+    ("scale near-tie: lower band 1000x too wide",
+     "int near_lo = dv - lo <= 1e-6 * dv;", "int near_lo = dv - lo <= 1e-3 * dv;", [NT]),
+    ("scale near-tie: upper band 1000x too wide",
+     "int near_hi = h != 0x7bff && hi - dv <= 1e-6 * dv;",
+     "int near_hi = h != 0x7bff && hi - dv <= 1e-3 * dv;", [NT]),
+    ("scale near-tie: a saturated scale taken to have an upper step",
+     "int near_hi = h != 0x7bff && hi - dv <= 1e-6 * dv;",
+     "int near_hi = hi - dv <= 1e-6 * dv;", [NT]),
+    ("scale near-tie: the step below a saturated scale ignored",
+     "int near_lo = dv - lo <= 1e-6 * dv;", "int near_lo = h != 0x7bff && dv - lo <= 1e-6 * dv;",
+     [NT]),
+    ("eviction near-tie: every candidate flagged",
+     "if (fabs(c[i].s - th) <= 1e-6 * fabs(th)) near[c[i].t] = 1;", "near[c[i].t] = 1;", [NT]),
+    ("eviction near-tie: no candidate flagged",
+     "if (fabs(c[i].s - th) <= 1e-6 * fabs(th)) near[c[i].t] = 1;", ";", [NT]),
+    ("eviction near-tie: band 1000x too wide",
+     "if (fabs(c[i].s - th) <= 1e-6 * fabs(th))", "if (fabs(c[i].s - th) <= 1e-3 * fabs(th))",
+     [NT]),
 ]
 
 
@@ -149,7 +181,7 @@ def test_every_planted_mistake_fails_a_pin(tmp_path):
         assert src.count(old) == 1, f"mutation site not unique or missing: {name}"
     clean = str(tmp_path / "clean.so")
     _build(src, clean)
-    assert _pins(clean, [NUM, E8, PATH]) == 0, "the pins fail on the unmodified oracle"
+    assert _pins(clean, [NUM, E8, PATH, NT]) == 0, "the pins fail on the unmodified oracle"
 
     def one(k):
         name, old, new, files = MUTANTS[k]
@@ -193,6 +225,21 @@ PY_MUTANTS = [
      "        x = x / math.sqrt(128.0)\n", "", LM),
     ("Lloyd-Max: decode restores RoPE with the wrong sign", "lloyd_max.py",
      "x[..., 64:] = hi * C + lo * S", "x[..., 64:] = hi * C - lo * S", LM),
+    ("Lloyd-Max scale near-tie: every group flagged", "lloyd_max.py",
+     "near |= abs(float(s32) - b) <= 1e-6 * float(s32)", "near |= True", NT),
+    ("Lloyd-Max scale near-tie: no group flagged", "lloyd_max.py",
+     "near |= abs(float(s32) - b) <= 1e-6 * float(s32)", "near |= False", NT),
+    ("Lloyd-Max scale near-tie: band 1000x too wide", "lloyd_max.py",
+     "near |= abs(float(s32) - b) <= 1e-6 * float(s32)",
+     "near |= abs(float(s32) - b) <= 1e-3 * float(s32)", NT),
+    ("Lloyd-Max threshold near-tie: every group flagged", "lloyd_max.py",
+     "near |= bool(np.any(np.abs(ui - t32) <= 1e-6 * np.maximum(1.0, np.abs(t32))))",
+     "near |= True", NT),
+    ("Lloyd-Max threshold near-tie: no group flagged", "lloyd_max.py",
+     "near |= bool(np.any(np.abs(ui - t32) <= 1e-6 * np.maximum(1.0, np.abs(t32))))",
+     "near |= False", NT),
+    ("Lloyd-Max threshold near-tie: band 1000x too wide", "lloyd_max.py",
+     "np.abs(ui - t32) <= 1e-6 * np.maximum", "np.abs(ui - t32) <= 1e-3 * np.maximum", NT),
 ]
 
 
@@ -222,7 +269,7 @@ def test_every_planted_mistake_in_the_numpy_oracles_fails_a_pin(tmp_path):
         assert srcs[mod].count(old) == 1, f"mutation site not unique or missing: {name}"
     clean = str(tmp_path / "clean")
     _tree(clean)
-    assert _py_pins(clean, ATT) == 0 and _py_pins(clean, LM) == 0, \
+    assert _py_pins(clean, ATT) == 0 and _py_pins(clean, LM) == 0 and _py_pins(clean, NT) == 0, \
         "the pins fail on the unmodified numpy oracles"
 
     def one(k):
