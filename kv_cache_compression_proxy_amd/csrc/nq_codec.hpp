@@ -215,7 +215,7 @@ struct TokenIn {
 // this lane's 8 fp16 dims of the row at position p (each K/V row is read once: streamed)
 __device__ __forceinline__ u32x4 load_row(const uint16_t *__restrict__ X, int p)
 {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(X + (uint32_t)p * kHeadDim));
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(X + (size_t)p * kHeadDim));
 }
 
 __device__ __forceinline__ void load_rope(const float *__restrict__ rope_cos,
@@ -306,15 +306,26 @@ __device__ __forceinline__ uint2 encode_token(const TokenIn &t, int g, float rho
         s16 = (uint32_t)m;
         sb32 = __float_as_uint(m * 0x1p-24f);
     }
-    // u = x / s up to a few ulps (x * (c * rcp(s)) instead of (x * c) / s): only a point
-    // within ~1e-6 of a Voronoi facet can change lattice point, and such points are ties
-    // (the butterflies leave group_sign(g) times the row in x; the factor restores the sign).
-    // A zero scale means an all-zero group: factor 0 keeps u = 0 (rcp(0) would make NaNs).
-    const float r = __builtin_amdgcn_rcpf(__uint_as_float(sb32));
-    const float f = s16 ? (kInvSqrt128 * group_sign(g)) * r : 0.0f;
+    // u = xn / s correctly rounded, xn = the normalised rotated value (x times the lane sign
+    // and 1/sqrt(128), rounded once): the lattice step sees exactly the oracle's input.
+    // r = 1/s rounded to nearest: v_rcp_f32 is within one ulp, and one Newton step with fused
+    // multiply-adds rounds it correctly for every binary16 s. With r correctly rounded and
+    // q0 = xn * r, the remainder xn - q0 * s is exact in one fma, and q0 + rem * r rounded
+    // once is the correctly rounded quotient (Markstein's division theorem). Both claims are
+    // checked exhaustively over the significands on the host. A zero scale (an all-zero
+    // group) takes r = 0, which keeps u = 0.
+    const float sf = __uint_as_float(sb32);
+    const float r0 = __builtin_amdgcn_rcpf(sf);
+    const float r1 = __builtin_fmaf(__builtin_fmaf(-sf, r0, 1.0f), r0, r0);
+    const float r = s16 ? r1 : 0.0f;
+    const float cs = kInvSqrt128 * group_sign(g);   // exact: +-fp32(1/sqrt(128))
     float u[8];
 #pragma unroll
-    for (int k = 0; k < 8; k++) u[k] = x[k] * f;
+    for (int k = 0; k < 8; k++) {
+        const float xn = x[k] * cs;
+        const float q0 = xn * r;
+        u[k] = __builtin_fmaf(__builtin_fmaf(-q0, sf, xn), r, q0);
+    }
     if (s16 == 0x7bffu) {   // saturated scale: |x / s| may exceed rho
 #pragma unroll
         for (int k = 0; k < 8; k++) u[k] = fminf(fmaxf(u[k], -rho), rho);
