@@ -47,43 +47,66 @@ def upload(w: kvsynth.Workload, tokens=None, chunk=8, only_layers=None):
     return K, V
 
 
+GUARD_BYTE = 0xA5
+
+
 class GpuRun:
     """Whole hot path on the GPU for parameters p and device K, V."""
 
-    def __init__(self, p: nq.NqParams, K, V, positions=None, decode=True, out_f32=True):
+    def __init__(self, p: nq.NqParams, K, V, positions=None, decode=True, out_f32=True,
+                 guard=False):
+        """guard: allocate every output with one more slot along its leading (layer) axis,
+        filled with a canary byte; guards_intact() then tells whether a call wrote past the
+        outputs' end."""
         self.p = p
         self.K, self.V, self.out_f32 = K, V, out_f32
         Lc = p.layer_end - p.layer_begin
         n = nq.nq_keep_count(p)
         self.n_keep = n
         dev = K.device
+        self._guards = []
         self.cos, self.sin = nq.rope_table(p, dev)
         T = p.tokens
-        self.scores = torch.full((max(Lc, 1), max(T, 1)), float("nan"), dtype=torch.float64,
-                                 device=dev)
+        self.scores = self._alloc((max(Lc, 1), max(T, 1)), torch.float64, dev, guard,
+                                  fill=float("nan"))
         if positions is None:
-            self.positions = torch.empty((max(Lc, 1), max(n, 1)), dtype=torch.int32, device=dev)
+            self.positions = self._alloc((max(Lc, 1), max(n, 1)), torch.int32, dev, guard)
             ws = nq.workspace(nq.nq_score_evict_workspace_bytes(p), dev)
             nq.nq_score_evict(p, K, self.positions, ws, scores=self.scores)
         else:
             self.positions = positions.to(dev).contiguous()
         H = p.kv_heads
-        self.codes_k = torch.empty((max(Lc, 1), H, max(n, 1), 128), dtype=torch.int8, device=dev)
-        self.codes_v = torch.empty_like(self.codes_k)
-        self.scales_k = torch.empty((max(Lc, 1), H, max(n, 1), 16), dtype=torch.float16,
-                                    device=dev)
-        self.scales_v = torch.empty_like(self.scales_k)
+        self.codes_k = self._alloc((max(Lc, 1), H, max(n, 1), 128), torch.int8, dev, guard)
+        self.codes_v = self._alloc((max(Lc, 1), H, max(n, 1), 128), torch.int8, dev, guard)
+        self.scales_k = self._alloc((max(Lc, 1), H, max(n, 1), 16), torch.float16, dev, guard)
+        self.scales_v = self._alloc((max(Lc, 1), H, max(n, 1), 16), torch.float16, dev, guard)
         nq.nq_encode(p, K, V, self.positions, self.cos, self.sin, self.codes_k, self.codes_v,
                      self.scales_k, self.scales_v)
         if decode:
             dt = torch.float32 if out_f32 else torch.float16
-            self.K_hat = torch.empty((max(Lc, 1), H, max(n, 1), 128), dtype=dt, device=dev)
-            self.V_hat = torch.empty_like(self.K_hat)
+            self.K_hat = self._alloc((max(Lc, 1), H, max(n, 1), 128), dt, dev, guard)
+            self.V_hat = self._alloc((max(Lc, 1), H, max(n, 1), 128), dt, dev, guard)
             self.dws = nq.workspace(nq.nq_decode_workspace_bytes(p), dev)
             nq.nq_decode(p, self.codes_k, self.codes_v, self.scales_k, self.scales_v,
                          self.positions, self.cos, self.sin, self.K_hat, self.V_hat,
                          nq.NQ_OUT_F32 if out_f32 else nq.NQ_OUT_F16, self.dws)
         torch.cuda.synchronize()
+
+    def _alloc(self, shape, dtype, dev, guard, fill=None):
+        if not guard:
+            t = torch.empty(shape, dtype=dtype, device=dev)
+            return t.fill_(fill) if fill is not None else t
+        full = torch.empty((shape[0] + 1,) + tuple(shape[1:]), dtype=dtype, device=dev)
+        body, tail = full[:shape[0]], full[shape[0]:]
+        if fill is not None:
+            body.fill_(fill)
+        tail.view(torch.uint8).fill_(GUARD_BYTE)
+        self._guards.append(tail)
+        return body
+
+    def guards_intact(self) -> bool:
+        torch.cuda.synchronize()
+        return all(bool(torch.all(g.view(torch.uint8) == GUARD_BYTE)) for g in self._guards)
 
     def lookback_error(self) -> int:
         """Spin-limit flag of the decode's tile look-back (0 when every wait ended normally)."""
@@ -97,6 +120,19 @@ def absolute_codes(d: np.ndarray) -> np.ndarray:
     return (((c + 128) % 256) - 128).astype(np.int8)
 
 
+def gpu_keep_set(scores: np.ndarray, T: int, W: int, n_keep: int) -> np.ndarray:
+    """The keep-set that the selection rule gives for the GPU's own scores: BOS, the window
+    [max(1, T-W), T) and the m best candidates t in [1, T-W) by (score descending, position
+    ascending), in ascending order. Certifies the selection exactly, whatever the scores."""
+    c_end = T - W
+    cand = np.arange(1, c_end) if c_end > 1 else np.zeros(0, np.int64)
+    prot = [0] + list(range(max(1, c_end), T)) if T > 0 else []
+    m = n_keep - len(prot)
+    sc = scores[cand].astype(np.float64)
+    order = np.lexsort((cand, -sc))           # -0.0 and +0.0 compare equal
+    return np.sort(np.concatenate([np.array(prot, np.int64), cand[order[:max(m, 0)]]]))
+
+
 def compare_keep(gpu_pos: np.ndarray, ora_pos: np.ndarray, near: np.ndarray):
     """-> (number of differing positions, all differences are eviction near-ties)."""
     a, b = set(gpu_pos.tolist()), set(ora_pos.tolist())
@@ -104,20 +140,74 @@ def compare_keep(gpu_pos: np.ndarray, ora_pos: np.ndarray, near: np.ndarray):
     return len(diff), all(near[t] for t in diff)
 
 
-def compare_codes(gc_abs, gs, oc_abs, os_, flags):
-    """Group-level comparison; -> (mismatching groups, mismatches that are not near-ties,
-    flagged groups)."""
+def is_e8_code(c: np.ndarray) -> bool:
+    """c = 2y for y in E8 = D8 u (D8 + 1/2): all c_i even with sum(c) = 0 mod 4 (y in D8), or
+    all odd with sum(c) = 0 mod 4 (y - 1/2 in D8)."""
+    c = c.astype(np.int64)
+    par = c & 1
+    return bool((np.all(par == 0) or np.all(par == 1)) and c.sum() % 4 == 0)
+
+
+def rotated_rows(X: np.ndarray, is_key: bool, pos: np.ndarray, Ct, St):
+    """x_of(h, j): the oracle's rotated row (RoPE removed for keys, normalised Hadamard) of kept
+    token j of head h, computed on demand."""
+    cache = {}
+
+    def x_of(h, j):
+        if (h, j) not in cache:
+            p = int(pos[j])
+            cache[(h, j)] = oracle.rotated_row(X[h, p], is_key, Ct[p] if is_key else None,
+                                               St[p] if is_key else None)
+        return cache[(h, j)]
+    return x_of
+
+
+def compare_codes(gc_abs, gs, oc_abs, os_, flags, x_of=None, bits=None):
+    """Group-level comparison; -> (mismatching groups, mismatches that are not Voronoi
+    near-ties, Voronoi-flagged groups). Scales must match bit for bit: the kernel's scale
+    arithmetic equals the oracle's on every input (checked exhaustively on the host), so the
+    oracle's scale near-tie flag (bit 1) excuses nothing here. With x_of and bits, every
+    mismatching group is also certified (see certify_group)."""
     gcode = gc_abs.reshape(gc_abs.shape[:-1] + (16, 8))
     ocode = oc_abs.reshape(oc_abs.shape[:-1] + (16, 8))
-    mism = np.any(gcode != ocode, axis=-1) | (gs.view(np.uint16) != os_.view(np.uint16))
-    bad = mism & (flags == 0)
-    return int(mism.sum()), int(bad.sum()), int((flags != 0).sum())
+    g16, o16 = gs.view(np.uint16), os_.view(np.uint16)
+    mism = np.any(gcode != ocode, axis=-1) | (g16 != o16)
+    vor = (flags & 1) != 0
+    bad = mism & ~vor
+    if x_of is not None:
+        for h, j, g in zip(*np.nonzero(mism)):
+            certify_group(x_of(h, j)[8 * g:8 * g + 8], gcode[h, j, g], int(g16[h, j, g]),
+                          ocode[h, j, g], int(o16[h, j, g]), int(flags[h, j, g]), bits,
+                          where=(int(h), int(j), int(g)))
+    return int(mism.sum()), int(bad.sum()), int(vor.sum())
+
+
+def certify_group(xg, c_gpu, s_gpu: int, c_ora, s_ora: int, flag: int, bits: int, where=()):
+    """A group where the GPU's code differs from the oracle's. Passes only if the difference is
+    one the tolerance rule allows and the GPU's answer is itself valid: the scales are equal,
+    the oracle flags a Voronoi near-tie, the GPU code is a point of E8 (c = 2y) inside the cube
+    |c_i| <= 2 rho + 1, and it is a nearest E8 point of the oracle's u up to the band (facet
+    distance of u - c/2 >= -band, band = 1e-6 * max(1, |u|_inf))."""
+    rho = (1 << (bits - 1)) - 1
+    c_gpu = np.asarray(c_gpu, np.int8)
+    assert s_gpu == s_ora, f"{where}: scales {s_gpu:#06x} / {s_ora:#06x} differ"
+    assert flag & 1, f"{where}: codes differ outside a Voronoi near-tie"
+    assert is_e8_code(c_gpu), f"{where}: GPU code {c_gpu.tolist()} is not an E8 point"
+    assert np.abs(c_gpu.astype(np.int64)).max() <= 2 * rho + 1, f"{where}: {c_gpu.tolist()}"
+    if s_gpu == 0:
+        assert not np.any(c_gpu), f"{where}: zero scale with nonzero code"
+        return
+    u, umax = oracle.group_u(xg, s_gpu, bits)
+    band = 1e-6 * max(1.0, float(umax))
+    m = oracle.e8_margin(u, c_gpu)
+    assert m >= -band, f"{where}: GPU point {c_gpu.tolist()} is {-m:.3g} outside its cell (band {band:.3g})"
 
 
 def recon_ratio(gpu_hat, ora_hat, scales, flags):
-    """max over token-heads without flagged groups of max|gpu - oracle| / max group scale."""
+    """max over token-heads without Voronoi-flagged groups (the only groups whose codes may
+    differ) of max|gpu - oracle| / max group scale."""
     s = scales.view(np.float16).astype(np.float64).max(axis=-1)
-    ok = ~np.any(flags != 0, axis=-1)
+    ok = ~np.any((flags & 1) != 0, axis=-1)
     err = np.abs(gpu_hat.astype(np.float64) - ora_hat).max(axis=-1)
     r = np.where(ok & (s > 0), err / np.where(s > 0, s, 1), 0.0)
     zero_rows = ok & (s == 0)
@@ -132,7 +222,7 @@ def fp16_recon_ratio(gpu16: np.ndarray, ora64: np.ndarray, scales, flags) -> flo
     half_ulp = 2.0 ** (np.floor(np.log2(mag)) - 11)
     excess = np.maximum(np.abs(g - ora64) - half_ulp, 0.0).max(axis=-1)
     s = scales.view(np.float16).astype(np.float64).max(axis=-1)
-    ok = ~np.any(flags != 0, axis=-1)
+    ok = ~np.any((flags & 1) != 0, axis=-1)
     r = np.where(ok, excess / np.where(s > 0, s, 1.0), 0.0)
     return float(r.max(initial=0.0))
 
@@ -147,5 +237,5 @@ def fp16_ulps(gpu16: np.ndarray, ora64: np.ndarray, flags=None) -> int:
     b = np.where(b & 0x8000, -(b & 0x7fff), b)
     d = np.abs(a - b).max(axis=-1)
     if flags is not None:
-        d = np.where(np.any(flags != 0, axis=-1), 0, d)
+        d = np.where(np.any((flags & 1) != 0, axis=-1), 0, d)
     return int(d.max(initial=0))

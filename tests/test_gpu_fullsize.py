@@ -31,9 +31,17 @@ def run_full(idx):
     p = params_of(w)
     say(f"[fullsize] {w.name}: generating {w.layers}x{w.kv_heads}x{w.tokens} fp16 K/V")
     K, V = upload(w)
+    prot = list(range(0, w.layer_begin)) + list(range(w.layer_end, w.layers))
+    saved = [(l, K[l].clone(), V[l].clone()) for l in prot]
     say(f"[fullsize] {w.name}: running score/evict/encode/decode")
-    run = GpuRun(p, K, V, out_f32=False)
+    run = GpuRun(p, K, V, out_f32=False, guard=True)
     assert run.lookback_error() == 0
+    # nothing written past any output, and the protected layers' K/V left as they were
+    assert run.guards_intact(), "a call wrote past the end of an output"
+    for l, k0, v0 in saved:
+        assert torch.equal(K[l].view(torch.int16), k0.view(torch.int16)), f"K layer {l} written"
+        assert torch.equal(V[l].view(torch.int16), v0.view(torch.int16)), f"V layer {l} written"
+    del saved
     return w, p, K, V, run
 
 
@@ -56,8 +64,9 @@ def test_fullsize_workload(idx):
     stats = check_sampled(w, p, run)
     assert all(s["keep_diff"] <= 2 for s in stats)
     if w.protect_boundary:
-        # protected layers are neither read nor written: their slices of the outputs do not
-        # exist (outputs are indexed by compressed layer) and K/V are left as they were
+        # outputs are indexed by compressed layer: the protected layers have no slice of them
+        # (run_full checked that their K/V bytes are unchanged and that the guard slots past
+        # every output are intact; test_gpu_protect checks that they are not read)
         assert run.codes_k.shape[0] == w.compressed_layers
 
 
