@@ -12,7 +12,8 @@
  * Conventions shared by every entry point
  *  - Tensors are dense, row-major, and live in device memory allocated by the caller (e.g.
  *    torch tensors). The library allocates no device memory and keeps no state between calls;
- *    calls on different streams with disjoint buffers may run concurrently.
+ *    calls on different streams with disjoint buffers may run concurrently. The one exception
+ *    is nq_decode_static, whose scratch is a fixed device array of the library (see there).
  *  - K and V are fp16 [layers][kv_heads][tokens][128] (the full cache, batch 1). Outputs are
  *    indexed by compressed layer lc = l - layer_begin, 0 <= lc < layer_end - layer_begin.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every call is
@@ -160,6 +161,27 @@ nq_status nq_decode(const nq_params *p, const int8_t *codes_k, const int8_t *cod
                     const void *scales_k, const void *scales_v, const int32_t *positions,
                     const float *rope_cos, const float *rope_sin, void *K_out, void *V_out,
                     nq_out_dtype out_dtype, void *workspace, size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory at all -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation: nq_decode with its scratch (tile tickets
+ * and look-back words) in a static device array of the library instead of a caller workspace.
+ * Same arguments, computation and outputs as nq_decode, minus the workspace; the call allocates
+ * nothing (no hipMalloc, no library routine that allocates).
+ *   - The array holds NQ_DECODE_STATIC_MAX_BYTES = 64 MiB on every GPU the library is loaded
+ *     on, until the process ends. Parameters whose nq_decode_workspace_bytes(p) exceed it are
+ *     rejected with NQ_ERR_WORKSPACE before any launch (64 MiB covers, e.g., 32 layers x 8 kv
+ *     heads x 26215 kept tokens; set NQ_VERBOSE for the sizes).
+ *   - The array is looked up once per device, on the first call with that device current;
+ *     `stream` must belong to the current device.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's contents (the
+ *     call clears what must start at zero itself). Calls that overlap on one GPU -- on two
+ *     streams, or from two host threads -- race and give invalid outputs: serialise them.
+ *   - The look-back spin-limit flag (word 1 of nq_decode's workspace) is not readable here. */
+#define NQ_DECODE_STATIC_MAX_BYTES ((size_t)64 << 20)
+nq_status nq_decode_static(const nq_params *p, const int8_t *codes_k, const int8_t *codes_v,
+                           const void *scales_k, const void *scales_v, const int32_t *positions,
+                           const float *rope_cos, const float *rope_sin, void *K_out,
+                           void *V_out, nq_out_dtype out_dtype, void *stream);
 
 /* One-token grouped-query attention over a reconstructed cache (consumer check; the VQKV page,
  * "推理流程集成", attends over reconstructed KV). Query head j reads kv head j / (q_heads / H):

@@ -36,7 +36,7 @@ EXPORTED = ("nq_keep_count", "nq_check_params", "nq_score_evict_workspace_bytes"
             "nq_score_evict", "nq_encode", "nq_decode", "nq_attend_decode",
             "nq_decode_attend_workspace_bytes", "nq_decode_attend",
             "nq_score_evict_attn_workspace_bytes", "nq_score_evict_attn", "nq_lloyd_max_table",
-            "nq_encode_scalar", "nq_decode_scalar", "nq_status_string")
+            "nq_encode_scalar", "nq_decode_scalar", "nq_decode_static", "nq_status_string")
 
 
 class NqParams(C.Structure):
@@ -71,8 +71,11 @@ _sig = {
     "nq_lloyd_max_table": (C.c_int, [C.c_int32, _v, _v]),
     "nq_encode_scalar": (C.c_int, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, _v]),
     "nq_decode_scalar": (C.c_int, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, C.c_int, _v]),
+    "nq_decode_static": (C.c_int, [_P, _v, _v, _v, _v, _v, _v, _v, _v, _v, C.c_int, _v]),
     "nq_status_string": (C.c_char_p, [C.c_int]),
 }
+# bytes of the static scratch array behind nq_decode_static (NQ_DECODE_STATIC_MAX_BYTES)
+NQ_DECODE_STATIC_MAX_BYTES = 64 << 20
 for _name, (_res, _args) in _sig.items():
     _fn = getattr(_lib, _name)
     _fn.restype = _res
@@ -236,6 +239,30 @@ def nq_decode(p, codes_k, codes_v, scales_k, scales_v, positions, rope_cos, rope
                                     _ptr(scales_v), _ptr(positions), _ptr(rope_cos),
                                     _ptr(rope_sin), _ptr(K_out), _ptr(V_out), out_dtype,
                                     _ptr(workspace), ws, _stream(stream)))
+
+
+def nq_decode_static(p, codes_k, codes_v, scales_k, scales_v, positions, rope_cos, rope_sin,
+                     K_out, V_out, out_dtype, stream=None):
+    """nq_decode without a workspace: the library's static device scratch (for callers that
+    cannot allocate; calls on one GPU must not overlap)."""
+    import torch
+    Lc, H, T, n = _sizes(p)
+    d = _dev(codes_k)
+    odt = torch.float32 if out_dtype == NQ_OUT_F32 else torch.float16
+    for name, t, dt, k in (("codes_k", codes_k, torch.int8, Lc * H * n * 128),
+                           ("codes_v", codes_v, torch.int8, Lc * H * n * 128),
+                           ("scales_k", scales_k, torch.float16, Lc * H * n * 16),
+                           ("scales_v", scales_v, torch.float16, Lc * H * n * 16),
+                           ("positions", positions, torch.int32, Lc * n),
+                           ("rope_cos", rope_cos, torch.float32, T * 64),
+                           ("rope_sin", rope_sin, torch.float32, T * 64),
+                           ("K_out", K_out, odt, Lc * H * n * 128),
+                           ("V_out", V_out, odt, Lc * H * n * 128)):
+        _need(t, name, dt, k, d)
+    _ok("nq_decode_static", _lib.nq_decode_static(
+        C.byref(p), _ptr(codes_k), _ptr(codes_v), _ptr(scales_k), _ptr(scales_v),
+        _ptr(positions), _ptr(rope_cos), _ptr(rope_sin), _ptr(K_out), _ptr(V_out), out_dtype,
+        _stream(stream)))
 
 
 def nq_attend_decode(p, Q, q_heads, K, V, n_tok, out, workspace, stream=None):

@@ -284,6 +284,46 @@ nq::ScalarArgs scalar_args(const nq_params *p, const int32_t *positions, const f
 
 }  // namespace
 
+// Scratch of nq_decode_static, for callers that cannot allocate (code under HIP graph capture,
+// serving loops, harnesses that forbid allocation): the decode's tile tickets and look-back
+// words live in this file-scope device array instead of a caller workspace. The module holds
+// it on every GPU it is loaded on until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: kernels and copies only ever get the address that
+// hipGetSymbolAddress returns for the current device.
+namespace {
+constexpr size_t kScratchBytes = NQ_DECODE_STATIC_MAX_BYTES;
+constexpr int kMaxDevices = 64;
+}
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per device (with that
+// device current) and kept.
+nq_status scratch_of_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return NQ_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return NQ_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            if (getenv("NQ_VERBOSE"))
+                fprintf(stderr, "libnq: hipGetSymbolAddress(scratch) on device %d: %s\n", dev,
+                        hipGetErrorString(e));
+            return NQ_ERR_HIP;
+        }
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return NQ_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int32_t nq_keep_count(const nq_params *p)
@@ -471,24 +511,40 @@ nq_status nq_encode(const nq_params *p, const void *K, const void *V, const int3
     return launched("nq_encode");
 }
 
-nq_status nq_decode(const nq_params *p, const int8_t *codes_k, const int8_t *codes_v,
-                    const void *scales_k, const void *scales_v, const int32_t *positions,
-                    const float *rope_cos, const float *rope_sin, void *K_out, void *V_out,
-                    nq_out_dtype out_dtype, void *workspace, size_t ws_bytes, void *stream)
+// Argument checks of nq_decode and nq_decode_static (everything but the workspace). *skip is
+// set when there is nothing to decode.
+static nq_status decode_args_ok(const nq_params *p, const int8_t *codes_k, const int8_t *codes_v,
+                                const void *scales_k, const void *scales_v,
+                                const int32_t *positions, const float *rope_cos,
+                                const float *rope_sin, void *K_out, void *V_out,
+                                nq_out_dtype out_dtype, bool *skip)
 {
+    *skip = false;
     nq_status st = check(p);
     if (st != NQ_OK) return st;
     if (out_dtype != NQ_OUT_F16 && out_dtype != NQ_OUT_F32) return NQ_ERR_INVALID_ARG;
-    const int32_t Lc = compressed_layers(p);
-    if (Lc == 0 || p->tokens == 0) return NQ_OK;
+    if (compressed_layers(p) == 0 || p->tokens == 0) {
+        *skip = true;
+        return NQ_OK;
+    }
     const void *ptrs16[] = {codes_k, codes_v, rope_cos, rope_sin, K_out, V_out};
     for (const void *q : ptrs16)
         if (!q || !aligned(q, 16)) return NQ_ERR_INVALID_ARG;
     if (!positions || !aligned(positions, 4) || !scales_k || !scales_v || !aligned(scales_k, 4) ||
         !aligned(scales_v, 4))
         return NQ_ERR_INVALID_ARG;
-    const size_t need = decode_ws(p, nullptr).bytes;
-    if (!workspace || ws_bytes < need || !aligned(workspace, kAlign)) return NQ_ERR_WORKSPACE;
+    return NQ_OK;
+}
+
+// The decode launches (look-back word reset, then the tiles) with the workspace at `workspace`
+// (validated by the caller).
+static nq_status decode_launch(const nq_params *p, const int8_t *codes_k, const int8_t *codes_v,
+                               const void *scales_k, const void *scales_v,
+                               const int32_t *positions, const float *rope_cos,
+                               const float *rope_sin, void *K_out, void *V_out,
+                               nq_out_dtype out_dtype, void *workspace, void *stream,
+                               const char *fn)
+{
     DecodeWs w = decode_ws(p, workspace);
     nq::CodecArgs a = codec_args(p, positions, rope_cos, rope_sin);
     a.codes_k = (int8_t *)codes_k;
@@ -507,7 +563,44 @@ nq_status nq_decode(const nq_params *p, const int8_t *codes_k, const int8_t *cod
     hipLaunchKernelGGL(nq::k_decode_reset, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0, s,
                        w.agg, words, w.ticket);
     hipLaunchKernelGGL(nq::k_decode, dim3((uint32_t)w.tiles), dim3(nq::kCodecThreads), 0, s, a);
-    return launched("nq_decode");
+    return launched(fn);
+}
+
+nq_status nq_decode(const nq_params *p, const int8_t *codes_k, const int8_t *codes_v,
+                    const void *scales_k, const void *scales_v, const int32_t *positions,
+                    const float *rope_cos, const float *rope_sin, void *K_out, void *V_out,
+                    nq_out_dtype out_dtype, void *workspace, size_t ws_bytes, void *stream)
+{
+    bool skip;
+    nq_status st = decode_args_ok(p, codes_k, codes_v, scales_k, scales_v, positions, rope_cos,
+                                  rope_sin, K_out, V_out, out_dtype, &skip);
+    if (st != NQ_OK || skip) return st;
+    const size_t need = decode_ws(p, nullptr).bytes;
+    if (!workspace || ws_bytes < need || !aligned(workspace, kAlign)) return NQ_ERR_WORKSPACE;
+    return decode_launch(p, codes_k, codes_v, scales_k, scales_v, positions, rope_cos, rope_sin,
+                         K_out, V_out, out_dtype, workspace, stream, "nq_decode");
+}
+
+nq_status nq_decode_static(const nq_params *p, const int8_t *codes_k, const int8_t *codes_v,
+                           const void *scales_k, const void *scales_v, const int32_t *positions,
+                           const float *rope_cos, const float *rope_sin, void *K_out,
+                           void *V_out, nq_out_dtype out_dtype, void *stream)
+{
+    bool skip;
+    nq_status st = decode_args_ok(p, codes_k, codes_v, scales_k, scales_v, positions, rope_cos,
+                                  rope_sin, K_out, V_out, out_dtype, &skip);
+    if (st != NQ_OK || skip) return st;
+    if (decode_ws(p, nullptr).bytes > kScratchBytes) {
+        if (getenv("NQ_VERBOSE"))
+            fprintf(stderr, "libnq nq_decode_static: needs %zu bytes of scratch, the static "
+                    "array holds %zu\n", decode_ws(p, nullptr).bytes, kScratchBytes);
+        return NQ_ERR_WORKSPACE;
+    }
+    void *ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != NQ_OK) return st;
+    return decode_launch(p, codes_k, codes_v, scales_k, scales_v, positions, rope_cos, rope_sin,
+                         K_out, V_out, out_dtype, ws, stream, "nq_decode_static");
 }
 
 size_t nq_decode_attend_workspace_bytes(const nq_params *p, int32_t q_heads)

@@ -190,3 +190,24 @@ def test_empty_caches_return_before_any_launch(case):
     else:
         assert L.nq_attend_decode(P, n, 4, n, n, 10, n, n, 0, n) == nq.NQ_OK
         assert L.nq_decode_attend(P, n, n, n, n, n, n, n, n, 4, n, n, 0, n) == nq.NQ_OK
+
+
+def test_static_decode_rejects_oversize_before_launch():
+    """nq_decode_static refuses parameters whose scratch exceeds its static array, and invalid
+    arguments, on the host (nothing is launched, no device is touched)."""
+    p = nq.make_params(32, 8, 131072, 512, 0, 2, 2, 1e4)
+    assert nq.nq_decode_workspace_bytes(p) > nq.NQ_DECODE_STATIC_MAX_BYTES
+    fake = 1 << 20
+    with pytest.raises(nq.NqError) as ei:
+        nq.nq_decode_static(p, *([fake] * 9), nq.NQ_OUT_F16, stream=0)
+    assert ei.value.status == nq.NQ_ERR_WORKSPACE
+    small = nq.make_params(1, 2, 100, 8, 600, 3, 2, 1e4)
+    with pytest.raises(nq.NqError) as ei:                        # misaligned codes
+        nq.nq_decode_static(small, fake + 1, *([fake] * 8), nq.NQ_OUT_F16, stream=0)
+    assert ei.value.status == nq.NQ_ERR_INVALID_ARG
+    with pytest.raises(nq.NqError) as ei:                        # bad output dtype
+        nq.nq_decode_static(small, *([fake] * 9), 5, stream=0)
+    assert ei.value.status == nq.NQ_ERR_INVALID_ARG
+    # nothing to decode: accepted without a launch
+    empty = nq.make_params(1, 2, 0, 8, 600, 3, 2, 1e4)
+    nq.nq_decode_static(empty, *([None] * 9), nq.NQ_OUT_F16, stream=0)
