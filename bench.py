@@ -55,6 +55,11 @@ def parse():
                          "and exit")
     ap.add_argument("--pmc-command", default="",
                     help="the profiling command, recorded in the summary")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "NAME"),
+                    help="write profiles/kernel_trace_<NAME>.md from a rocprofv3 --kernel-trace "
+                         "--stats run's kernel_stats.csv (the command given by --pmc-command) "
+                         "and exit")
+    ap.add_argument("--title", default="", help="title line of a --summarize-trace summary")
     ap.add_argument("--attn-score", action="store_true",
                     help="time the attention-weight scorer (nq_score_evict_attn, 32 query heads, "
                          "W-query observation window) against the key-key proxy scorer on the "
@@ -158,6 +163,30 @@ def summarize_pmc(args, w, decode_step: bool = False):
         lines.append(f"traffic {ph} {int(round(tot))}")
     lines += [f"kernel-sources {kernel_source_hash()}", "```", ""]
     out = traffic_path(w, decode_step)
+    open(out, "w").write("\n".join(lines))
+    log(f"[bench] wrote {out}")
+
+
+def summarize_trace(args):
+    """rocprofv3 kernel stats CSV -> profiles/kernel_trace_<name>.md (per-kernel calls and
+    durations)."""
+    import csv
+    rows = list(csv.DictReader(open(args.summarize_trace[0])))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    name = args.summarize_trace[1]
+    lines = [f"# rocprofv3 kernel stats: {args.title or name}", "",
+             "Command (from /tmp, with TMPDIR=/tmp; `$REPO` is the repository root):", "", "```",
+             args.pmc_command or "(not recorded)", "```", "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['Name'][:120]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    lines += ["", "Kernels outside `nq::` belong to bench.py itself (torch's fills and copies of "
+              "inputs; in a headline run also the 1 GiB device copy timed as the achievable "
+              "line); the shares include them.", "",
+              f"Kernel sources: {kernel_source_hash()}", ""]
+    out = os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md")
     open(out, "w").write("\n".join(lines))
     log(f"[bench] wrote {out}")
 
@@ -597,6 +626,7 @@ def decode_step(args):
     kv16 = kept * 2 * 256                                  # fp16 K+V the step attends over
     alg_f = kept * (2 * 128 + 2 * 32) + Lc * n * 4 + T * 64 * 4 * 2 + Lc * Hq * (256 + 512)
     alg_2 = kept * (2 * 128 + 2 * 32 + 2 * 256) * 1 + kept * 2 * 256 + Lc * n * 4 + T * 512
+    alg_dec = kept * (2 * 128 + 2 * 32 + 2 * 256) + Lc * n * 4 + T * 512
     achieved = alg_f / (ms_f * 1e-3) / 1e9
     res = {
         "metric": "one-token GQA decode step over the compressed cache: fp16-KV GB/s attended",
@@ -626,6 +656,14 @@ def decode_step(args):
                      "algorithmic_bytes_per_launch": alg_f, "avg_launch_ms": round(ms_f, 4)},
         "two_call_algorithmic_frac_of_peak": round(alg_2 / (ms_2 * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                                                    4),
+        # nq_decode alone on this cache (the decode direction of the long-context workload):
+        # codes + scales in, fp16 K/V out
+        "decode_only": {
+            "ms": round(ms_dec, 4),
+            "fp16_KV_GBps": round(kv16 / (ms_dec * 1e-3) / 1e9, 2),
+            "algorithmic_bytes": alg_dec,
+            "algorithmic_frac_of_peak": round(alg_dec / (ms_dec * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        },
     }
     print(json.dumps(res), flush=True)
 
@@ -639,6 +677,9 @@ def main():
         sys.exit(2)
     import kvsynth
     w = kvsynth.workload(args.workload)
+    if args.summarize_trace:
+        summarize_trace(args)
+        return
     if args.summarize_pmc:
         if args.decode_step:
             summarize_pmc(args, kvsynth.workload(2), decode_step=True)

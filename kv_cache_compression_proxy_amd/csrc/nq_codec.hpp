@@ -827,7 +827,10 @@ __device__ void decode_tile(const CodecArgs &a, int lc, int h, int tile, int tic
 // tile-major over the chains: tile k of a chain holds ticket k * chains + chain, so its
 // predecessor started `chains` tickets earlier and has usually published its inclusive prefix
 // by the time it is looked up (a chain-major order would start a chain's tiles together and
-// make the last ones walk back through many tile sums).
+// make the last ones walk back through many tile sums). Chain index = lc + Lc (tensor + 2 h):
+// a ticket's class, and with it the block's XCD, follows the layer (chains = 2 Lc H), so the
+// kv heads of one layer -- which share its kept positions -- read their rotary rows through
+// the same L2 instead of one XCD per head.
 __global__ __launch_bounds__(kCodecThreads) void k_decode(CodecArgs a)
 {
     __shared__ int s_ticket;
@@ -837,10 +840,11 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode(CodecArgs a)
     const int ticket = s_ticket;
     const int tile = ticket / chains;
     uint32_t r = ticket % chains;
-    const int h = r % a.H;
-    r /= a.H;
+    const uint32_t Lc = (uint32_t)chains / (2u * (uint32_t)a.H);
+    const int lc = r % Lc;
+    r /= Lc;
     const int tensor = r & 1;
-    const int lc = r >> 1;
+    const int h = r >> 1;
     __shared__ DecodeShared sh;
     if (tensor == 0)
         decode_tile<true>(a, lc, h, tile, ticket, chains, sh);

@@ -119,7 +119,7 @@ __device__ __forceinline__ bool row_sum_reporter(int l)
 }
 
 // grid: pairs * tiles blocks (pairs = Lc * H); tickets tile-major over the pairs as in
-// k_decode. Look-back slots: 2 * ticket + tensor (K = 0, V = 1).
+// k_decode, layer-fastest. Look-back slots: 2 * ticket + tensor (K = 0, V = 1).
 template <int G>
 __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
 {
@@ -130,8 +130,12 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
     __syncthreads();
     const int ticket = s_ticket;
     const int tile = ticket / pairs;
-    const int pair = ticket % pairs;
-    const int h = pair % a.H, lc = pair / a.H;
+    // ticket slot lc + Lc h: the kv heads of a layer (same kept positions, same rotary rows)
+    // share a ticket class and so an XCD and its L2; `pair` is the storage index lc * H + h
+    const int tp = ticket % pairs;
+    const int Lcf = pairs / a.H;
+    const int lc = tp % Lcf, h = tp / Lcf;
+    const int pair = lc * a.H + h;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane_group(lane & 15), q = wave * 4 + (lane >> 4);

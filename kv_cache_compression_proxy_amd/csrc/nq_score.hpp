@@ -480,4 +480,188 @@ __global__ __launch_bounds__(kSelThreads) void k_select_reg(const double *__rest
     }
 }
 
+// ---- selection for long layers, candidate flags in LDS ----------------------------------------
+// The same selection for layers of at most KPT * 1024 candidates whose keys do not fit in
+// registers: the radix passes re-read the scores (L2-resident) as k_select does, but the
+// candidates' outcome -- above the selected key, or equal to it -- is kept as one bit per chunk
+// and thread in LDS after a single further pass, and the ordered emission ranks kept positions with
+// wave ballots and one block scan over the (chunk, wave) counts, as k_select_reg does (k_select
+// instead scans the whole position range in 4096-position steps, two block scans per step).
+// Chunk u of thread tid is position 1 + tid + 1024 u.
+
+// exclusive scan of n counts in LDS, kPer per thread (n <= kPer * 1024); returns the total
+template <int kPer>
+__device__ __forceinline__ uint32_t scan_counts(uint32_t *cnt, int n, uint32_t *s_wave)
+{
+    const int tid = threadIdx.x;
+    uint32_t loc[kPer], sum = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; e++) {
+        const int idx = tid * kPer + e;
+        loc[e] = idx < n ? cnt[idx] : 0u;
+        sum += loc[e];
+    }
+    uint32_t tot;
+    uint32_t base = block_excl_scan(sum, s_wave, tot);   // its barriers order the reads above
+#pragma unroll
+    for (int e = 0; e < kPer; e++) {
+        const int idx = tid * kPer + e;
+        if (idx < n) cnt[idx] = base;
+        base += loc[e];
+    }
+    __syncthreads();
+    return tot;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__restrict__ scores,
+                                                            int T, int W, int n_keep,
+                                                            int32_t *__restrict__ positions)
+{
+    constexpr int kWaves = kSelThreads / 64;
+    constexpr int kWords = (KPT + 31) / 32;
+    constexpr int kCnt = KPT * kWaves;
+    constexpr int kPer = (kCnt + kSelThreads - 1) / kSelThreads;
+    constexpr int kBatch = 8;
+    static_assert(KPT % kBatch == 0, "whole batches of loads");
+    __shared__ SelectShared sh;
+    __shared__ uint32_t s_cnt[kCnt];
+    __shared__ uint32_t s_gt[kWords][kSelThreads], s_eq[kWords][kSelThreads];
+    const int lc = blockIdx.x;
+    const double *s = scores + (size_t)lc * T;
+    int32_t *out = positions + (size_t)lc * n_keep;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c_end = T - W;
+    const int n_cand = c_end > 1 ? c_end - 1 : 0;
+    const int m = n_keep - (T - n_cand);
+    const bool partial = m > 0 && m < n_cand;
+
+    if (tid == 0) { sh.prefix = 0ull; sh.mask = 0ull; sh.krem = m; sh.all = 0; sh.bits = 64; }
+    if (partial) {
+        uint64_t kmin = ~0ull, kmax = 0ull;
+#pragma unroll 1
+        for (int u0 = 0; u0 < KPT; u0 += kBatch) {
+            double v[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; b++) {
+                const int t = 1 + tid + (u0 + b) * kSelThreads;
+                v[b] = t < c_end ? s[t] : 0.0;
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; b++) {
+                if (1 + tid + (u0 + b) * kSelThreads < c_end) {
+                    const uint64_t k = order_key(v[b]);
+                    kmin = k < kmin ? k : kmin;
+                    kmax = k > kmax ? k : kmax;
+                }
+            }
+        }
+        sel_init_prefix(sh, kmin, kmax);
+    }
+    __syncthreads();
+    if (partial) {
+        for (int top = sh.bits; top > 0; top -= 8) {
+            const int shift = top >= 8 ? top - 8 : 0;
+            const uint32_t dmask = top >= 8 ? 255u : ((1u << top) - 1u);
+            sel_clear_hist(sh);
+            const uint64_t prefix = sh.prefix, mask = sh.mask;
+    #pragma unroll 1
+        for (int u0 = 0; u0 < KPT; u0 += kBatch) {
+                double v[kBatch];
+#pragma unroll
+                for (int b = 0; b < kBatch; b++) {
+                    const int t = 1 + tid + (u0 + b) * kSelThreads;
+                    v[b] = t < c_end ? s[t] : 0.0;
+                }
+#pragma unroll
+                for (int b = 0; b < kBatch; b++) {
+                    const uint64_t k = order_key(v[b]);
+                    if (1 + tid + (u0 + b) * kSelThreads < c_end && (k & mask) == prefix)
+                        sel_count(sh, k, shift, dmask);
+                }
+            }
+            sel_pick_digit(sh, shift, dmask, prefix, mask);
+            if (sh.all) break;
+        }
+    }
+    const uint64_t prefix = sh.prefix, mask = sh.mask;
+    const int krem = sh.krem;
+    const bool take_all_eq = sh.all != 0;
+    const uint64_t below = (1ull << lane) - 1ull;
+    // bit u of word u / 32: chunk u's candidate is above the selected key (gt) or equal (eq)
+    // per-thread flag words in LDS ([word][thread]: conflict-free), so no register array is
+    // indexed by a loop variable
+    for (int w = 0; w < kWords; w++) {
+        uint32_t g1 = 0u, e1 = 0u;
+#pragma unroll 1
+        for (int u0 = 0; u0 < 32; u0 += kBatch) {
+            double v[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; b++) {
+                const int t = 1 + tid + (32 * w + u0 + b) * kSelThreads;
+                v[b] = (partial && t < c_end) ? s[t] : 0.0;
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; b++) {
+                const uint32_t f = 1u << (u0 + b);
+                if (1 + tid + (32 * w + u0 + b) * kSelThreads < c_end) {
+                    if (!partial) {
+                        if (m > 0) g1 |= f;
+                    } else {
+                        const uint64_t k = order_key(v[b]) & mask;
+                        if (k > prefix) g1 |= f;
+                        else if (k == prefix) e1 |= f;
+                    }
+                }
+            }
+        }
+        s_gt[w][tid] = g1;
+        s_eq[w][tid] = e1;
+    }
+    // rank the ties in position order, keep the first krem of them (or all)
+    if (partial && !take_all_eq) {
+        for (int u = 0; u < KPT; u++) {
+            const uint64_t b = __ballot((s_eq[u >> 5][tid] >> (u & 31)) & 1u);
+            if (lane == 0) s_cnt[u * kWaves + wave] = (uint32_t)__popcll(b);
+        }
+        __syncthreads();
+        scan_counts<kPer>(s_cnt, kCnt, sh.wave_sum);
+        for (int w = 0; w < kWords; w++) {
+            const uint32_t e1 = s_eq[w][tid];
+            uint32_t add = 0u;
+            for (int bb = 0; bb < 32; bb++) {
+                const uint32_t bit = (e1 >> bb) & 1u;
+                const uint64_t b = __ballot(bit);
+                const uint32_t r = s_cnt[(32 * w + bb) * kWaves + wave] + (uint32_t)__popcll(b & below);
+                if (bit && r < (uint32_t)krem) add |= 1u << bb;
+            }
+            s_gt[w][tid] |= add;
+        }
+        __syncthreads();
+    } else {
+        for (int w = 0; w < kWords; w++) s_gt[w][tid] |= s_eq[w][tid];
+    }
+    // output ranks of the kept candidates; BOS first, the window after the candidates
+    for (int u = 0; u < KPT; u++) {
+        const uint64_t b = __ballot((s_gt[u >> 5][tid] >> (u & 31)) & 1u);
+        if (lane == 0) s_cnt[u * kWaves + wave] = (uint32_t)__popcll(b);
+    }
+    __syncthreads();
+    const uint32_t kept = scan_counts<kPer>(s_cnt, kCnt, sh.wave_sum);
+    for (int u = 0; u < KPT; u++) {
+        const uint32_t bit = (s_gt[u >> 5][tid] >> (u & 31)) & 1u;
+        const uint64_t b = __ballot(bit);
+        if (bit) {
+            const uint32_t o = 1u + s_cnt[u * kWaves + wave] + (uint32_t)__popcll(b & below);
+            if (o < (uint32_t)n_keep) out[o] = 1 + tid + u * kSelThreads;
+        }
+    }
+    if (tid == 0 && T > 0 && n_keep > 0) out[0] = 0;
+    const int ws = c_end > 1 ? c_end : 1;               // first window position after BOS
+    for (int t = ws + tid; t < T; t += kSelThreads) {
+        const uint32_t o = 1u + kept + (uint32_t)(t - ws);
+        if (o < (uint32_t)n_keep) out[o] = t;
+    }
+}
+
 }  // namespace nq

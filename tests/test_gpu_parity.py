@@ -146,10 +146,15 @@ EDGE = [
     ("small-keep", 1, 8, 40, 3, 900, 3, 2, 1e4, 0, 1),
     ("single-head-long", 1, 1, 20000, 128, 600, 3, 2, 1e4, 0, 1),
     ("tile-exact", 1, 4, 640, 0, 600, 3, 2, 1e4, 0, 1),       # n_keep = 256
-    # the selection's two kernels: 32768 candidates (the most the register-resident one
-    # takes) and 32769 (the one that re-reads the scores)
+    # the selection's three kernels: 32768 candidates (the most the register-resident one
+    # takes), 32769 and 131072 (the one with flags in LDS), 131073 (the one that re-reads the
+    # scores for the emission too)
     ("select-32768-candidates", 1, 1, 33025, 256, 600, 3, 2, 1e4, 0, 1),
     ("select-32769-candidates", 1, 1, 33026, 256, 600, 3, 2, 1e4, 0, 1),
+    ("select-131072-candidates", 1, 1, 131329, 256, 800, 2, 2, 1e4, 0, 1),
+    ("select-131073-candidates", 1, 1, 131330, 256, 800, 2, 2, 1e4, 0, 1),
+    # zero window over more than 32768 candidates: every score ties (position order decides)
+    ("no-window-ties-long", 1, 2, 40000, 0, 600, 3, 2, 1e4, 0, 1),
 ]
 
 
