@@ -117,3 +117,25 @@ def test_scores_equal_double_sum_over_window_and_heads():
             assert abs(s[t] - ref) <= 1e-12 * max(1.0, abs(ref))
         else:
             assert np.isnan(s[t])
+
+
+@pytest.mark.parametrize("base", [1e4, 1e6])
+def test_rope_table_matches_transformers_llama_rotary(base):
+    """The model convention from a library: transformers' LlamaRotaryEmbedding (split-half
+    layout, inv_freq = base^(-2i/d) with d = 128, computed there in fp32). Its cos/sin over the
+    first 256 positions equal the oracle's table to within that library's fp32 angle error, and
+    its two halves repeat the 64 frequencies (pairs i and i + 64)."""
+    transformers = pytest.importorskip("transformers")
+    import torch
+    from transformers.models.llama.modeling_llama import LlamaRotaryEmbedding
+    cfg = transformers.LlamaConfig(hidden_size=1024, num_attention_heads=8, head_dim=128,
+                                   rope_theta=base, max_position_embeddings=4096)
+    rot = LlamaRotaryEmbedding(config=cfg)
+    P = 256
+    c, s = rot(torch.zeros(1, P, 128), torch.arange(P)[None])
+    c, s = c[0].double().numpy(), s[0].double().numpy()
+    assert np.array_equal(c[:, :64], c[:, 64:]) and np.array_equal(s[:, :64], s[:, 64:])
+    C, S = oracle.rope_table(P, base)
+    # fp32 angles p * inv_freq in the library: |error| <= ~P * 2^-24
+    assert np.abs(c[:, :64] - C).max() < 4e-5
+    assert np.abs(s[:, :64] - S).max() < 4e-5

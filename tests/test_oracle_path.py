@@ -5,6 +5,8 @@ CPU only."""
 import json
 import os
 
+import itertools
+
 import numpy as np
 import pytest
 import torch
@@ -240,3 +242,48 @@ def test_nominal_ratio_closed_form():
     assert 16 / b["bits"] == pytest.approx(b["value"], abs=5e-3)
     bare = (2 * 128 * 16) / (128 * 2 * b["bits"])
     assert bare == pytest.approx(b["value"], abs=5e-3)
+
+
+def _codebook_size(bits: int) -> int:
+    """E8 points y with |y_i| <= rho + 1/2 (every point the quantizer can emit), counted by
+    brute force over the integer and half-integer cubes for b = 2, and by the parity generating
+    function otherwise: n integer vectors in [-rho, rho]^8 with even sum plus half-integer ones
+    whose sum of (y_i - 1/2) is even."""
+    rho = (1 << (bits - 1)) - 1
+    if bits == 2:
+        ints = np.array(list(itertools.product(range(-rho, rho + 1), repeat=8)))
+        halves = np.array(list(itertools.product(range(-rho - 1, rho + 1), repeat=8)))
+        return int(np.sum(ints.sum(1) % 2 == 0) + np.sum(halves.sum(1) % 2 == 0))
+    n_int = 2 * rho + 1                       # values -rho..rho; sum of (-1)^v over them is -1
+    n_half = 2 * rho + 2                      # z = y - 1/2 in -rho-1..rho; sum of (-1)^z is 0
+    return (n_int ** 8 + 1) // 2 + n_half ** 8 // 2
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_codebook_size_fits_the_budget(bits):
+    n = _codebook_size(bits)
+    assert 2 ** (8 * bits - 1) < n <= 2 ** (8 * bits)        # 8b bits index a group, no fewer
+    if bits == 2:
+        assert n == 36049
+    if bits == 3:
+        assert n == 11271009
+
+
+def test_nominal_ratio_counted_from_the_oracle_output():
+    """The nominal ratio from what the oracle actually emits for a layer: each 8-float group as
+    a fixed-length index into its codebook (ceil(log2 size) bits, the size counted above), the
+    fp16 scale arrays and the int32 positions, in bytes as produced; against the fp16 cache's
+    2 * H * T * 128 * 16 bits."""
+    w = kvsynth.workload(0).with_(tokens=600)
+    K, V = kvsynth.layer_kv(w, 0)
+    C, S = oracle.rope_table(w.tokens, w.rope_base)
+    enc = oracle.compress_layer(K, V, w.window, w.evict_permille, w.bits_k, w.bits_v, C, S)
+    H, n = w.kv_heads, enc["positions"].size
+    groups = H * n * 16                                          # per tensor
+    code_bits = groups * sum(int(np.ceil(np.log2(_codebook_size(b))))
+                             for b in (w.bits_k, w.bits_v))
+    other_bits = 8 * (enc["scales_k"].nbytes + enc["scales_v"].nbytes + enc["positions"].nbytes)
+    assert enc["positions"].dtype == np.int32 and enc["scales_k"].dtype == np.uint16
+    ratio = (2 * H * w.tokens * 128 * 16) / (code_bits + other_bits)
+    assert oracle.nominal_ratio(H, w.tokens, n, w.bits_k, w.bits_v) == pytest.approx(ratio,
+                                                                                       rel=1e-12)
