@@ -95,7 +95,7 @@ int32_t codec_tiles(const nq_params *p) { return (keep_count(p) + nq::kCodecTile
 int32_t decode_tiles(const nq_params *p) { return (keep_count(p) + nq::kDecTile - 1) / nq::kDecTile; }
 
 // Per-layer selection: the register-resident kernel when a layer's candidates fit it (up to
-// 32 keys per thread), the one with per-chunk flags in registers up to 128 chunks per thread,
+// 32 keys per thread), the one with per-chunk flags in LDS up to 64 or 128 chunks per thread,
 // else the one that re-reads the scores on every pass and for the emission.
 constexpr int kSelRegKeys = 32;
 constexpr int kSelMemChunks = 128;
@@ -106,6 +106,9 @@ void launch_select(const double *scores, int32_t T, int32_t W, int32_t n_keep, i
     if (n_cand <= kSelRegKeys * nq::kSelThreads)
         hipLaunchKernelGGL(nq::k_select_reg<kSelRegKeys>, dim3(Lc), dim3(nq::kSelThreads), 0, s,
                            scores, T, W, n_keep, positions);
+    else if (n_cand <= kSelMemChunks / 2 * nq::kSelThreads)
+        hipLaunchKernelGGL(nq::k_select_mem<kSelMemChunks / 2>, dim3(Lc), dim3(nq::kSelThreads),
+                           0, s, scores, T, W, n_keep, positions);
     else if (n_cand <= kSelMemChunks * nq::kSelThreads)
         hipLaunchKernelGGL(nq::k_select_mem<kSelMemChunks>, dim3(Lc), dim3(nq::kSelThreads), 0,
                            s, scores, T, W, n_keep, positions);

@@ -522,8 +522,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
     constexpr int kWords = (KPT + 31) / 32;
     constexpr int kCnt = KPT * kWaves;
     constexpr int kPer = (kCnt + kSelThreads - 1) / kSelThreads;
+    // loads in flight per thread on every pass (16 or 32 measured no faster)
     constexpr int kBatch = 8;
-    static_assert(KPT % kBatch == 0, "whole batches of loads");
+    static_assert(KPT % kBatch == 0 && 32 % kBatch == 0, "whole batches of loads");
     __shared__ SelectShared sh;
     __shared__ uint32_t s_cnt[kCnt];
     __shared__ uint32_t s_gt[kWords][kSelThreads], s_eq[kWords][kSelThreads];

@@ -19,7 +19,10 @@ from test_gpu_parity import check_layer
 pytestmark = pytest.mark.gpu
 
 ATT_TOL = 1e-3   # max|gpu - oracle| / max|v_hat| per (layer, query head)
-FUSED_FULL_TOL = 1e-4   # the fused path at 26K tokens (fp32 sums against fp64)
+# the fused path at 26K tokens (fp32 sums against the oracle's fp64): each 256-token tile sums
+# w (c + 64) and removes 64 W once, so its partial carries ~log2(80 / 16) more bits of rounding
+# than a sum of w c would; observed ~5e-6 of max|v_hat|
+FUSED_FULL_TOL = 2e-5
 
 
 def sampled_layers(n):
@@ -84,9 +87,13 @@ def test_fullsize_longctx_and_decode_step():
     fused = nq.attend_compressed(c, Q, check=True)
     torch.cuda.synchronize()
     Ct, St = oracle.rope_table(w.tokens, w.rope_base)
+    G = Q.shape[1] // w.kv_heads
     for lc in (0, w.compressed_layers - 1):
         say(f"[decode-step] oracle attention on layer {lc}")
         K_l, V_l = kvsynth.layer_kv(w, lc)
+        # 1. the consumer check: against the oracle's own compression of the layer (its
+        #    keep-set and codes may differ from the GPU's in certified near-ties; one swapped
+        #    token moves the output by about its softmax weight, ~1/n)
         enc = oracle.compress_layer(K_l, V_l, w.window, w.evict_permille, w.bits_k, w.bits_v,
                                     Ct, St)
         Kh, Vh = oracle.decode_layer(enc["codes_k"], enc["codes_v"], enc["scales_k"],
@@ -96,15 +103,27 @@ def test_fullsize_longctx_and_decode_step():
         Vh16 = Vh.astype(np.float16).astype(np.float64)
         ref = oracle.attend_layer(Q[lc].cpu().numpy(), Kh16, Vh16)
         got = out[lc].cpu().numpy().astype(np.float64)
-        G = Q.shape[1] // w.kv_heads
         vmax = np.abs(Vh16).max(axis=(1, 2)).repeat(G)
         err = np.abs(got - ref).max(axis=1) / vmax
         say(f"[decode-step] layer {lc}: max err / max|v| = {err.max():.3g}")
         assert err.max() <= ATT_TOL
-        # the fused path, from the same compressed cache, against the oracle's attention over
-        # its fp64 reconstruction (the fused path rounds nothing to fp16)
-        reff = oracle.attend_layer(Q[lc].cpu().numpy(), Kh, Vh)
+        # 2. the kernels' own arithmetic: the oracle decodes the GPU's compressed layer
+        #    (positions, codes, scales as the GPU wrote them) and attends over it in fp64; the
+        #    fused path against that, the two-call path against its fp16 rounding
+        n = run.n_keep
+        Kg, Vg = oracle.decode_layer(run.codes_k[lc].cpu().numpy()[:, :n],
+                                     run.codes_v[lc].cpu().numpy()[:, :n],
+                                     run.scales_k[lc].cpu().numpy()[:, :n],
+                                     run.scales_v[lc].cpu().numpy()[:, :n],
+                                     run.positions[lc].cpu().numpy()[:n], Ct, St)
+        reff = oracle.attend_layer(Q[lc].cpu().numpy(), Kg, Vg)
+        vmaxg = np.abs(Vg).max(axis=(1, 2)).repeat(G)
         gotf = fused[lc].cpu().numpy().astype(np.float64)
-        errf = np.abs(gotf - reff).max(axis=1) / np.abs(Vh).max(axis=(1, 2)).repeat(G)
+        errf = np.abs(gotf - reff).max(axis=1) / vmaxg
         say(f"[decode-step] fused, layer {lc}: max err / max|v| = {errf.max():.3g}")
         assert errf.max() <= FUSED_FULL_TOL
+        ref16 = oracle.attend_layer(Q[lc].cpu().numpy(), Kg.astype(np.float16).astype(np.float64),
+                                    Vg.astype(np.float16).astype(np.float64))
+        err2 = np.abs(got - ref16).max(axis=1) / vmaxg
+        say(f"[decode-step] two-call on the GPU's codes, layer {lc}: {err2.max():.3g}")
+        assert err2.max() <= FUSED_FULL_TOL
