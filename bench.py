@@ -60,6 +60,9 @@ def parse():
                          "--stats run's kernel_stats.csv (the command given by --pmc-command) "
                          "and exit")
     ap.add_argument("--title", default="", help="title line of a --summarize-trace summary")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "NAME"),
+                    help="write profiles/counters_<NAME>.md from a rocprofv3 --pmc run of SQ "
+                         "instruction counters (the command given by --pmc-command) and exit")
     ap.add_argument("--attn-score", action="store_true",
                     help="time the attention-weight scorer (nq_score_evict_attn, 32 query heads, "
                          "W-query observation window) against the key-key proxy scorer on the "
@@ -187,6 +190,46 @@ def summarize_trace(args):
               "line); the shares include them.", "",
               f"Kernel sources: {kernel_source_hash()}", ""]
     out = os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md")
+    open(out, "w").write("\n".join(lines))
+    log(f"[bench] wrote {out}")
+
+
+def summarize_counters(args):
+    """rocprofv3 SQ counter CSV -> profiles/counters_<name>.md: per-dispatch averages of the
+    instruction counters of the library's kernels."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    d = args.summarize_counters[0]
+    for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+        if "nq::" not in r["Kernel_Name"]:
+            continue
+        name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("nq::", "").strip()
+        vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    cols = [("SQ_WAVES", "waves", 1.0, "{:.0f}"), ("SQ_INSTS_VALU", "VALU instr (M)", 1e-6, "{:.1f}"),
+            ("SQ_INSTS_VMEM_RD", "VMEM rd instr (M)", 1e-6, "{:.2f}"),
+            ("SQ_INSTS_VMEM_WR", "VMEM wr instr (M)", 1e-6, "{:.2f}"),
+            ("SQ_WAVE_CYCLES", "wave cycles (M)", 1e-6, "{:.0f}"),
+            ("SQ_WAIT_INST_ANY", "waiting wave cycles (M)", 1e-6, "{:.0f}"),
+            ("GRBM_GUI_ACTIVE", "GPU busy cycles (M, all XCDs)", 1e-6, "{:.2f}")]
+    name = args.summarize_counters[1]
+    lines = [f"# Instruction counters: {args.title or name}", "",
+             "Per-dispatch averages of rocprofv3 SQ counters over the run's dispatches of each "
+             "kernel. `VALU ms (4 cyc)` = SQ_INSTS_VALU x 4 cycles / (1024 SIMDs x 2.4 GHz): "
+             "the time if every VALU instruction took the 4 issue cycles of a wave64 instruction "
+             "on a 16-lane SIMD (plain fp32 add/mul, integer and bitwise ops issue in about half "
+             "that on this chip, so this bounds the VALU time from above).", "",
+             "Command (from /tmp with TMPDIR=/tmp; `$REPO` is the repository root):", "", "```",
+             args.pmc_command or "(not recorded)", "```", "",
+             "| kernel | " + " | ".join(c[1] for c in cols) + " | VALU ms (4 cyc) |",
+             "|---|" + "---|" * (len(cols) + 1)]
+    for k in sorted(vals):
+        m = {c: sum(v) / len(v) for c, v in vals[k].items()}
+        cells = [fmt.format(m[c] * sc) if c in m else "" for c, _, sc, fmt in cols]
+        valu_ms = m.get("SQ_INSTS_VALU", 0.0) * 4 / (1024 * 2.4e9) * 1e3
+        lines.append(f"| {k} | " + " | ".join(cells) + f" | {valu_ms:.3f} |")
+    lines += ["", f"Kernel sources: {kernel_source_hash()}", ""]
+    out = os.path.join(ROOT, "profiles", f"counters_{name}.md")
     open(out, "w").write("\n".join(lines))
     log(f"[bench] wrote {out}")
 
@@ -679,6 +722,9 @@ def main():
     w = kvsynth.workload(args.workload)
     if args.summarize_trace:
         summarize_trace(args)
+        return
+    if args.summarize_counters:
+        summarize_counters(args)
         return
     if args.summarize_pmc:
         if args.decode_step:
