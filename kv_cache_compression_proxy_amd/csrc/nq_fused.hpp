@@ -118,6 +118,16 @@ __device__ __forceinline__ bool row_sum_reporter(int l)
     return (l & (G == 1 ? 15 : G == 2 ? 7 : G == 4 ? 3 : 1)) == 0;
 }
 
+// Two code bytes of a running word (offset form c + 64, picked by the v_perm selector sel) as
+// exact fp16 values c: under the exponent byte 0x64 a byte b is the fp16 1024 + b, and one
+// packed add of -1088 leaves c (|c| <= 16, so every step is exact).
+__device__ __forceinline__ f16x2 codes_f16(uint32_t word, uint32_t sel)
+{
+    uint32_t h = __builtin_amdgcn_perm(0x64646464u, word, sel);
+    asm("v_pk_add_f16 %0, %0, %1" : "+v"(h) : "s"(0xE440E440u));
+    return __builtin_bit_cast(f16x2, h);
+}
+
 // grid: pairs * tiles blocks (pairs = Lc * H); tickets tile-major over the pairs as in
 // k_decode, layer-fastest. Look-back slots: 2 * ticket + tensor (K = 0, V = 1).
 template <int G>
@@ -189,9 +199,9 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
                 float d[G];
 #pragma unroll
                 for (int hq = 0; hq < G; hq++) {
-                    d[hq] = 0.0f;
+                    d[hq] = qv[hq][0] * x[0];
 #pragma unroll
-                    for (int k = 0; k < 8; k++) d[hq] = __builtin_fmaf(qv[hq][k], x[k], d[hq]);
+                    for (int k = 1; k < 8; k++) d[hq] = __builtin_fmaf(qv[hq][k], x[k], d[hq]);
                 }
                 const float z = row_sums<G>(d, lane & 15);
                 if (row_sum_reporter<G>(lane & 15)) sh.z[jl][row_sum_index<G>(lane & 15)] = z;
@@ -226,16 +236,16 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
     }
     __syncthreads();   // also: every key row has been read, the staging area may be reused
 
-    // ---- values: acc[i][k] = sum_t p_t,i * (s_t / 2) * (c_t,k + 64), W[i] = sum_t p_t,i s_t / 2
+    // ---- values: acc[i][k] = sum_t p_t,i * (s_t / 2) * c_t,k, on the codes themselves: each
+    //      code is an exact fp16, and one v_fma_mix_f32 per (head, dim) multiplies it by the
+    //      fp32 weight and adds to the fp32 accumulator with one rounding
     stage_tile<kFusedRun>(a.codes_v, a.scales_v, row0, nt, nullptr, a.T, sh.u.t.delta, sh.u.t.scale,
                nullptr);
-    float acc[G][8], W[G];
+    float acc[G][8];
 #pragma unroll
-    for (int i = 0; i < G; i++) {
-        W[i] = 0.0f;
+    for (int i = 0; i < G; i++)
 #pragma unroll
         for (int k = 0; k < 8; k++) acc[i][k] = 0.0f;
-    }
     {
         uint2 run = tile_run_base<kFusedRun>(sh.u.t.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
                                   2 * (size_t)ticket + 1, 2 * (size_t)pairs, tile,
@@ -249,27 +259,19 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
             if (jl < jend) {
                 run = run_step(run, sd[jl * 16]);
                 const float hs = 0.5f * h2f(sl[jl * kGroups + g]);
-                float b[8];
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    b[k] = (float)((run.x >> (8 * k)) & 0xffu);
-                    b[k + 4] = (float)((run.y >> (8 * k)) & 0xffu);
-                }
+                const f16x2 c01 = codes_f16(run.x, 0x04010400u), c23 = codes_f16(run.x, 0x04030402u);
+                const f16x2 c45 = codes_f16(run.y, 0x04010400u), c67 = codes_f16(run.y, 0x04030402u);
+                const float c[8] = {(float)c01.x, (float)c01.y, (float)c23.x, (float)c23.y,
+                                    (float)c45.x, (float)c45.y, (float)c67.x, (float)c67.y};
 #pragma unroll
                 for (int hq = 0; hq < G; hq++) {
                     const float w = sh.z[jl][hq] * hs;
-                    W[hq] += w;
 #pragma unroll
-                    for (int k = 0; k < 8; k++) acc[hq][k] = __builtin_fmaf(w, b[k], acc[hq][k]);
+                    for (int k = 0; k < 8; k++) acc[hq][k] = __builtin_fmaf(c[k], w, acc[hq][k]);
                 }
             }
         }
     }
-    // remove the +64 offset: acc = sum w (c + 64) - 64 sum w
-#pragma unroll
-    for (int hq = 0; hq < G; hq++)
-#pragma unroll
-        for (int k = 0; k < 8; k++) acc[hq][k] = __builtin_fmaf(-64.0f, W[hq], acc[hq][k]);
     // sum over the 4 rows of the wave (lane distance 16, 32), then over the 4 waves in LDS
 #pragma unroll
     for (int msk = 16; msk < 64; msk <<= 1)

@@ -4,8 +4,9 @@ The GPU is fed the oracle's own compressed layers (codes, scales, positions from
 oracle.compress_layer), so only the fused kernel is under test. The oracle's reference is its
 decode (oracle.decode_layer, fp64) followed by its attention (oracle.attend_layer, fp64) over
 those reconstructions, with no fp16 rounding in between -- the fused path never materialises
-K_hat/V_hat. Tolerance: max |gpu - oracle| / max |v_hat| per (layer, query head) <= 1e-5 (fp32
-scores, exponentials and sums against fp64; the attention check's own bar is 1e-3).
+K_hat/V_hat. Tolerance: max |gpu - oracle| / max |v_hat| per (layer, query head) <= 1e-6 (fp32
+scores, exponentials and sums against fp64: a few dozen roundings of 2^-24 on the way to each
+output, observed <= 1.3e-7; the attention check's own bar is 1e-3).
 """
 import numpy as np
 import pytest
@@ -18,7 +19,7 @@ from gpu_helpers import say
 
 pytestmark = pytest.mark.gpu
 
-FUSED_TOL = 1e-5
+FUSED_TOL = 1e-6
 
 # (tokens, window, evict_permille, G, layers, protect_boundary): several 128-token tiles with a
 # ragged tail, a single partial tile, a tile holding one token, a one-token cache, and a

@@ -19,10 +19,12 @@ from test_gpu_parity import check_layer
 pytestmark = pytest.mark.gpu
 
 ATT_TOL = 1e-3   # max|gpu - oracle| / max|v_hat| per (layer, query head)
-# the fused path at 26K tokens (fp32 sums against the oracle's fp64): each 256-token tile sums
-# w (c + 64) and removes 64 W once, so its partial carries ~log2(80 / 16) more bits of rounding
-# than a sum of w c would; observed ~5e-6 of max|v_hat|
-FUSED_FULL_TOL = 2e-5
+# the fused path at 26K tokens against the oracle's fp64 decode and attention of the same
+# compressed layer (fp32 scores, exponentials and weighted code sums; observed ~1.5e-7)
+FUSED_FULL_TOL = 2e-6
+# the two-call path against the same, both reconstructions rounded to fp16 (a one-ulp binary16
+# difference in a reconstructed element moves the output by up to ~5e-4 of it; observed ~3e-6)
+TWO_CALL_FULL_TOL = 2e-5
 
 
 def sampled_layers(n):
@@ -126,4 +128,4 @@ def test_fullsize_longctx_and_decode_step():
                                     Vg.astype(np.float16).astype(np.float64))
         err2 = np.abs(got - ref16).max(axis=1) / vmaxg
         say(f"[decode-step] two-call on the GPU's codes, layer {lc}: {err2.max():.3g}")
-        assert err2.max() <= FUSED_FULL_TOL
+        assert err2.max() <= TWO_CALL_FULL_TOL
