@@ -735,10 +735,23 @@ __device__ __forceinline__ void stage_tile(const int8_t *codes, const uint16_t *
     if (pos && tid < nt) s_pos[tid] = min(max(pv, 0), T - 1);
 }
 
-// The running code of this lane's group just before lane group q's first token of a staged
-// tile (q walks tile rows q * RUN ..), offset-64 (c + 64 per byte). Synchronises the block
-// before reading the tile and after the look-back; slot/step/err as in chain_lookback.
-template <int RUN>
+// This lane's 8 delta bytes of staged tile row jl: dims 8g..8g+7 (one uint2), or with SPLIT
+// dims 4g..4g+3 and 64+4g..64+4g+3 (two dwords of the 128-byte row)
+template <bool SPLIT>
+__device__ __forceinline__ uint2 lane_delta(const uint4 *s_delta, int jl, int g)
+{
+    if (SPLIT) {
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(s_delta) + jl * 32 + g;
+        return make_uint2(w[0], w[16]);
+    }
+    return reinterpret_cast<const uint2 *>(s_delta)[jl * 16 + g];
+}
+
+// The running code of this lane's 8 dims (see lane_delta) just before lane group q's first
+// token of a staged tile (q walks tile rows q * RUN ..), offset-64 (c + 64 per byte).
+// Synchronises the block before reading the tile and after the look-back; slot/step/err as in
+// chain_lookback. Every tile of a chain must use the same partition of the dims over lanes.
+template <int RUN, bool SPLIT = false>
 __device__ __forceinline__ uint2 tile_run_base(const uint4 *s_delta, int nt, int q, int g,
                                                uint2 (*s_tot)[16], uint2 *s_excl,
                                                uint32_t *lb_agg, uint32_t *lb_incl, size_t slot,
@@ -747,12 +760,11 @@ __device__ __forceinline__ uint2 tile_run_base(const uint4 *s_delta, int nt, int
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // 1. the sum of this lane group's deltas (offset-64)
     __syncthreads();
-    const uint2 *sd = reinterpret_cast<const uint2 *>(s_delta) + g;   // [token][16 lanes]
     uint2 acc = make_uint2(kOff64, kOff64);
 #pragma unroll
     for (int i = 0; i < RUN; i++) {
         const int jl = q * RUN + i;
-        if (jl < nt) acc = run_step(acc, sd[jl * 16]);
+        if (jl < nt) acc = run_step(acc, lane_delta<SPLIT>(s_delta, jl, g));
     }
     // 2. prefix over the lane groups before this one: across the 4 rows of a wave with lane
     //    shuffles, then across the 4 waves through LDS (one barrier); group 15's lanes then

@@ -31,8 +31,12 @@ struct FusedArgs {
 
 // a tile partial per query head: running max, sum of weights, then 128 accumulated dims
 constexpr int kPartStride = 2 + kHeadDim;
-constexpr int kFusedRun = 16;                  // tokens per lane group
+// 12 tokens per lane group: a 192-token tile's staging (about 35 KB of LDS) lets four blocks
+// share a CU, as many as the kernel's 128 VGPRs allow
+constexpr int kFusedRun = 12;                  // tokens per lane group
 constexpr int kFusedTile = 16 * kFusedRun;     // tokens per block
+static_assert(kFusedTile % 64 == 0, "the tile softmax gives every lane kFusedTile / 64 rows");
+constexpr int kRotAhead = 2;                  // keys: rotary rows requested this many tokens ahead
 
 template <int G>
 struct FusedShared {
@@ -118,6 +122,73 @@ __device__ __forceinline__ bool row_sum_reporter(int l)
     return (l & (G == 1 ? 15 : G == 2 ? 7 : G == 4 ? 3 : 1)) == 0;
 }
 
+__device__ __forceinline__ void load_f32x4(const float *__restrict__ p, float x[4])
+{
+    const float4 v = *reinterpret_cast<const float4 *>(p);
+    x[0] = v.x, x[1] = v.y, x[2] = v.z, x[3] = v.w;
+}
+
+// One key row in the fused kernel's key layout: lane g holds dims 4g + m (x[m]) and
+// 64 + 4g + m (x[4 + m]), m = 0..3, so both members of each RoPE pair (i, i + 64) sit in one
+// lane. code: the running code bytes of those dims (offset form c + 64; .x the low dims, .y the
+// high ones); hs_lo, hs_hi: (s / 2) / sqrt(128) for their groups g / 2 and 8 + g / 2; (cr, sr):
+// the rotary table row of the token's position at dims 4g..4g+3. Returns x = group_sign(g)
+// times the reconstructed key, K = RoPE(H y) with H the normalised Hadamard transform.
+//
+// The Hadamard stages commute, so they run in the order this layout makes cheap: h = 1, 2 on
+// the integer codes in packed fp16 (exact, as in decode_row), the scale, h = 4, 8, 16, 32 across
+// lanes (partners g ^ 1, g ^ 2, g ^ 4, g ^ 8, the butterflies of hadamard_cross_lane), and
+// h = 64 inside the lane fused with the rotation: with (a, b) = the pair before stage 64,
+//   k_i      = (a + b) C - (a - b) S = a (C - S) + b (C + S),
+//   k_{i+64} = (a - b) C + (a + b) S = a (C + S) - b (C - S).
+__device__ __forceinline__ void decode_key_split(int g, uint2 code, float hs_lo, float hs_hi,
+                                                 const float cr[4], const float sr[4], float x[8])
+{
+    uint32_t q0 = __builtin_amdgcn_perm(0x64646464u, code.x, 0x04010400u);   // (c0, c1)
+    uint32_t q1 = __builtin_amdgcn_perm(0x64646464u, code.x, 0x04030402u);   // (c2, c3)
+    uint32_t q2 = __builtin_amdgcn_perm(0x64646464u, code.y, 0x04010400u);   // (c4, c5)
+    uint32_t q3 = __builtin_amdgcn_perm(0x64646464u, code.y, 0x04030402u);   // (c6, c7)
+    uint32_t r0, r1, r2, r3;
+    asm("v_pk_add_f16 %0, %0, %4\n"
+        "v_pk_add_f16 %1, %1, %4\n"
+        "v_pk_add_f16 %2, %2, %4\n"
+        "v_pk_add_f16 %3, %3, %4\n"
+        // h = 1: (a, b) -> (a + b, a - b) inside each register
+        "v_pk_add_f16 %0, %0, %0 op_sel:[0,1] op_sel_hi:[0,1] neg_hi:[0,1]\n"
+        "v_pk_add_f16 %1, %1, %1 op_sel:[0,1] op_sel_hi:[0,1] neg_hi:[0,1]\n"
+        "v_pk_add_f16 %2, %2, %2 op_sel:[0,1] op_sel_hi:[0,1] neg_hi:[0,1]\n"
+        "v_pk_add_f16 %3, %3, %3 op_sel:[0,1] op_sel_hi:[0,1] neg_hi:[0,1]\n"
+        : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3)
+        : "s"(0xE440E440u));   // (-1088, -1088)
+    // h = 2 within each half: q0 = (y0, y1), q1 = (y2, y3) -> (z0, z2), (z1, z3); same above
+    asm("v_pk_add_f16 %0, %4, %5 op_sel:[0,0] op_sel_hi:[0,0] neg_hi:[0,1]\n"
+        "v_pk_add_f16 %1, %4, %5 op_sel:[1,1] op_sel_hi:[1,1] neg_hi:[0,1]\n"
+        "v_pk_add_f16 %2, %6, %7 op_sel:[0,0] op_sel_hi:[0,0] neg_hi:[0,1]\n"
+        "v_pk_add_f16 %3, %6, %7 op_sel:[1,1] op_sel_hi:[1,1] neg_hi:[0,1]\n"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(q0), "v"(q1), "v"(q2), "v"(q3));
+    // fp16 sums times fp32 scale, one rounding each
+    asm("v_fma_mix_f32 %0, %8, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %2, %8, %12, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %1, %9, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %3, %9, %12, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %4, %10, %13, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %6, %10, %13, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %5, %11, %13, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
+        "v_fma_mix_f32 %7, %11, %13, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
+          "=&v"(x[6]), "=&v"(x[7])
+        : "v"(r0), "v"(r1), "v"(r2), "v"(r3), "v"(hs_lo), "v"(hs_hi));
+    hadamard_cross_lane(x, g);   // stages h = 4..32; x = group_sign(g) * (the row before h = 64)
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+        const float A = cr[m] - sr[m], B = cr[m] + sr[m];
+        const float a = x[m], b = x[4 + m];
+        x[m] = __builtin_fmaf(b, B, a * A);
+        x[4 + m] = __builtin_fmaf(-b, A, a * B);
+    }
+}
+
 // Two code bytes of a running word (offset form c + 64, picked by the v_perm selector sel) as
 // exact fp16 values c: under the exponent byte 0x64 a byte b is the fp16 1024 + b, and one
 // packed add of -1088 leaves c (|c| <= 16, so every step is exact).
@@ -155,16 +226,23 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
     const int jl0 = q * kFusedRun;                     // this lane group's first tile row
     const size_t row0 = (size_t)pair * n_keep + t0;    // chain row of the tile's first token
 
-    // queries of this kv head, this lane's 8 dims, times group_sign(g) / sqrt(128): the keys
-    // come out of decode_row with group_sign(g) applied, so q . x is the true score
+    // queries of this kv head in the key layout of decode_key_split (this lane's dims 4g..4g+3
+    // and 64+4g..64+4g+3), times group_sign(g) / sqrt(128): the keys come out with
+    // group_sign(g) applied, so q . x is the true score
     float qv[G][8];
     {
         const float f = group_sign(g) * kInvSqrt128;
 #pragma unroll
         for (int i = 0; i < G; i++) {
-            load_f16x8(a.Q + ((size_t)lc * a.Hq + h * G + i) * kHeadDim + 8 * g, qv[i]);
+            const uint16_t *qp = a.Q + ((size_t)lc * a.Hq + h * G + i) * kHeadDim + 4 * g;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(qp);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(qp + 64);
+            const uint32_t w[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-            for (int k = 0; k < 8; k++) qv[i][k] *= f;
+            for (int k = 0; k < 4; k++) {
+                qv[i][2 * k] = h2f(w[k] & 0xffffu) * f;
+                qv[i][2 * k + 1] = h2f(w[k] >> 16) * f;
+            }
         }
     }
 
@@ -172,40 +250,46 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
     stage_tile<kFusedRun>(a.codes_k, a.scales_k, row0, nt, a.positions + (size_t)lc * n_keep + t0, a.T,
                sh.u.t.delta, sh.u.t.scale, sh.pos);
     {
-        uint2 run = tile_run_base<kFusedRun>(sh.u.t.delta, nt, q, g, sh.tot, sh.excl, a.lb_agg, a.lb_incl,
-                                  2 * (size_t)ticket, 2 * (size_t)pairs, tile,
-                                  a.lb_ticket + kTicketErr);
-        const uint2 *sd = reinterpret_cast<const uint2 *>(sh.u.t.delta) + g;
+        uint2 run = tile_run_base<kFusedRun, true>(sh.u.t.delta, nt, q, g, sh.tot, sh.excl,
+                                                   a.lb_agg, a.lb_incl, 2 * (size_t)ticket,
+                                                   2 * (size_t)pairs, tile,
+                                                   a.lb_ticket + kTicketErr);
         const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.u.t.scale);
-        const int jend = min(nt, jl0 + kFusedRun);
-        float rc[2][8], rs[2][8];   // rotary rows of the current and the next token
-        if (jl0 < jend) {
-            const size_t p = (size_t)sh.pos[jl0] * 64 + 8 * (g & 7);
-            load_f32x8(a.rope_cos + p, rc[0]);
-            load_f32x8(a.rope_sin + p, rs[0]);
+        const float hsf = 0.5f * kInvSqrt128;
+        // Every lane group walks kFusedRun rows. Rows past the tile's end (only in a chain's
+        // last, partial tile) are computed on the last row's data and not reported, so the loop
+        // has no branch around a load: the rotary rows of token i + kRotAhead are requested while
+        // token i is computed, with exact waits.
+        float rc[kRotAhead + 1][4], rs[kRotAhead + 1][4];
+#pragma unroll
+        for (int i = 0; i < kRotAhead; i++) {
+            const size_t p = (size_t)sh.pos[min(jl0 + i, nt - 1)] * 64 + 4 * g;
+            load_f32x4(a.rope_cos + p, rc[i]);
+            load_f32x4(a.rope_sin + p, rs[i]);
         }
 #pragma unroll
         for (int i = 0; i < kFusedRun; i++) {
-            const int jl = jl0 + i, cur = i & 1;
-            if (jl < jend) {
-                if (jl + 1 < jend) {
-                    const size_t p = (size_t)sh.pos[jl + 1] * 64 + 8 * (g & 7);
-                    load_f32x8(a.rope_cos + p, rc[cur ^ 1]);
-                    load_f32x8(a.rope_sin + p, rs[cur ^ 1]);
-                }
-                run = run_step(run, sd[jl * 16]);
-                float x[8];
-                decode_row<true>(g, run, sl[jl * kGroups + g], rc[cur], rs[cur], x);
-                float d[G];
-#pragma unroll
-                for (int hq = 0; hq < G; hq++) {
-                    d[hq] = qv[hq][0] * x[0];
-#pragma unroll
-                    for (int k = 1; k < 8; k++) d[hq] = __builtin_fmaf(qv[hq][k], x[k], d[hq]);
-                }
-                const float z = row_sums<G>(d, lane & 15);
-                if (row_sum_reporter<G>(lane & 15)) sh.z[jl][row_sum_index<G>(lane & 15)] = z;
+            const int jl = jl0 + i, jr = min(jl, nt - 1), cur = i % (kRotAhead + 1);
+            if (i + kRotAhead < kFusedRun) {
+                const int nx = (i + kRotAhead) % (kRotAhead + 1);
+                const size_t p = (size_t)sh.pos[min(jl + kRotAhead, nt - 1)] * 64 + 4 * g;
+                load_f32x4(a.rope_cos + p, rc[nx]);
+                load_f32x4(a.rope_sin + p, rs[nx]);
             }
+            run = run_step(run, lane_delta<true>(sh.u.t.delta, jr, g));
+            const float hs_lo = hsf * h2f(sl[jr * kGroups + (g >> 1)]);
+            const float hs_hi = hsf * h2f(sl[jr * kGroups + 8 + (g >> 1)]);
+            float x[8];
+            decode_key_split(g, run, hs_lo, hs_hi, rc[cur], rs[cur], x);
+            float d[G];
+#pragma unroll
+            for (int hq = 0; hq < G; hq++) {
+                d[hq] = qv[hq][0] * x[0];
+#pragma unroll
+                for (int k = 1; k < 8; k++) d[hq] = __builtin_fmaf(qv[hq][k], x[k], d[hq]);
+            }
+            const float z = row_sums<G>(d, lane & 15);
+            if (jl < nt && row_sum_reporter<G>(lane & 15)) sh.z[jl][row_sum_index<G>(lane & 15)] = z;
         }
     }
     __syncthreads();
@@ -227,7 +311,7 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
 #pragma unroll
         for (int r = 0; r < kRows; r++) {
             const float pr = lane + 64 * r < nt ? expf(zr[r] - m) : 0.0f;
-            if (lane + 64 * r < nt) sh.z[lane + 64 * r][hq] = pr;
+            sh.z[lane + 64 * r][hq] = pr;   // 0 past the tile's end
             l += pr;
         }
 #pragma unroll
@@ -252,23 +336,21 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
                                   a.lb_ticket + kTicketErr);
         const uint2 *sd = reinterpret_cast<const uint2 *>(sh.u.t.delta) + g;
         const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.u.t.scale);
-        const int jend = min(nt, jl0 + kFusedRun);
+        // rows past the tile's end (as in the key loop) read the last row and carry weight 0
 #pragma unroll
         for (int i = 0; i < kFusedRun; i++) {
-            const int jl = jl0 + i;
-            if (jl < jend) {
-                run = run_step(run, sd[jl * 16]);
-                const float hs = 0.5f * h2f(sl[jl * kGroups + g]);
-                const f16x2 c01 = codes_f16(run.x, 0x04010400u), c23 = codes_f16(run.x, 0x04030402u);
-                const f16x2 c45 = codes_f16(run.y, 0x04010400u), c67 = codes_f16(run.y, 0x04030402u);
-                const float c[8] = {(float)c01.x, (float)c01.y, (float)c23.x, (float)c23.y,
-                                    (float)c45.x, (float)c45.y, (float)c67.x, (float)c67.y};
+            const int jl = jl0 + i, jr = min(jl, nt - 1);
+            run = run_step(run, sd[jr * 16]);
+            const float hs = 0.5f * h2f(sl[jr * kGroups + g]);
+            const f16x2 c01 = codes_f16(run.x, 0x04010400u), c23 = codes_f16(run.x, 0x04030402u);
+            const f16x2 c45 = codes_f16(run.y, 0x04010400u), c67 = codes_f16(run.y, 0x04030402u);
+            const float c[8] = {(float)c01.x, (float)c01.y, (float)c23.x, (float)c23.y,
+                                (float)c45.x, (float)c45.y, (float)c67.x, (float)c67.y};
 #pragma unroll
-                for (int hq = 0; hq < G; hq++) {
-                    const float w = sh.z[jl][hq] * hs;
+            for (int hq = 0; hq < G; hq++) {
+                const float w = sh.z[jl][hq] * hs;
 #pragma unroll
-                    for (int k = 0; k < 8; k++) acc[hq][k] = __builtin_fmaf(c[k], w, acc[hq][k]);
-                }
+                for (int k = 0; k < 8; k++) acc[hq][k] = __builtin_fmaf(c[k], w, acc[hq][k]);
             }
         }
     }

@@ -21,13 +21,13 @@ pytestmark = pytest.mark.gpu
 
 FUSED_TOL = 1e-6
 
-# (tokens, window, evict_permille, G, layers, protect_boundary): several 128-token tiles with a
-# ragged tail, a single partial tile, a tile holding one token, a one-token cache, and a
+# (tokens, window, evict_permille, G, layers, protect_boundary): several 192-token tiles with a
+# ragged tail, a single partial tile, a last tile holding one token, a one-token cache, and a
 # protected-boundary layer range (layer 1 of 3 compressed)
 CASES = [
     (2048, 128, 600, 4, 2, 0),
     (300, 64, 600, 1, 1, 0),
-    (129, 16, 0, 2, 1, 0),
+    (193, 16, 0, 2, 1, 0),
     (1, 4, 600, 8, 1, 0),
     (1000, 32, 800, 8, 3, 1),
 ]
