@@ -52,7 +52,8 @@ typedef enum nq_out_dtype {
 typedef struct nq_params {
     int32_t layers;           /* L >= 1 */
     int32_t kv_heads;         /* H >= 1 */
-    int32_t tokens;           /* T >= 0 (prefill length) */
+    int32_t tokens;           /* T >= 0 (prefill length); above 8388607 unsupported (a layer's
+                                 rows of one head are addressed with 32-bit byte offsets) */
     int32_t head_dim;         /* must be 128 */
     int32_t layer_begin;      /* compressed layer range [layer_begin, layer_end) */
     int32_t layer_end;

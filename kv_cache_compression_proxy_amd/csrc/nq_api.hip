@@ -42,8 +42,9 @@ nq_status check(const nq_params *p)
         return NQ_ERR_INVALID_ARG;
     if (p->head_dim != 128) return NQ_ERR_UNSUPPORTED;
     if (p->bits_k > 4 || p->bits_v > 4) return NQ_ERR_UNSUPPORTED;
-    // 32-bit token and tile indices inside the kernels
-    if ((int64_t)p->tokens * 16 > INT32_MAX) return NQ_ERR_UNSUPPORTED;
+    // 32-bit token and tile indices inside the kernels, and 32-bit byte offsets of a token's
+    // row within one head of one layer (256 bytes per fp16 row or fp32 rotary row)
+    if ((int64_t)p->tokens * 256 > INT32_MAX) return NQ_ERR_UNSUPPORTED;
     if ((int64_t)p->kv_heads * 2 * compressed_layers(p) * ((int64_t)p->tokens / nq::kDecTile + 1) >
         INT32_MAX)
         return NQ_ERR_UNSUPPORTED;

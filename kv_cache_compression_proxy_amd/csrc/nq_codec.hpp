@@ -236,6 +236,38 @@ __device__ __forceinline__ void load_token(const float *__restrict__ rope_cos,
     if (IS_KEY) load_rope(rope_cos, rope_sin, p, g, t);
 }
 
+// One chain's encode inputs and code output as buffer resources: a token's row and rotary rows
+// sit at 32-bit byte offsets p * 256 (+ the lane's part) from the resource bases, which costs
+// one shift per token instead of 64-bit address arithmetic for every pointer. Offsets past a
+// resource's size read zeros and drop writes; every offset used here is in range.
+constexpr int kBufWord3 = 0x00020000;   // raw 32-bit dword access, the gfx9 family's word 3
+constexpr int kBufNt = 2;               // cache policy: non-temporal (streamed once)
+
+struct ChainBuf {
+    __amdgpu_buffer_rsrc_t x, cos, sin, codes;
+};
+
+template <bool IS_KEY>
+__device__ __forceinline__ void load_token_buf(const ChainBuf &b, int p, int g, TokenIn &t)
+{
+    const uint32_t o = (uint32_t)p << 8;   // 128 fp16 dims or 64 fp32 rotary values per token
+    t.v = __builtin_amdgcn_raw_buffer_load_b128(b.x, o | (uint32_t)(16 * g), 0, kBufNt);
+    if (IS_KEY) {
+        const uint32_t r = o | (uint32_t)(32 * (g & 7));
+        const u32x4 c0 = __builtin_amdgcn_raw_buffer_load_b128(b.cos, r, 0, 0);
+        const u32x4 c1 = __builtin_amdgcn_raw_buffer_load_b128(b.cos, r + 16, 0, 0);
+        const u32x4 s0 = __builtin_amdgcn_raw_buffer_load_b128(b.sin, r, 0, 0);
+        const u32x4 s1 = __builtin_amdgcn_raw_buffer_load_b128(b.sin, r + 16, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            t.c[k] = __uint_as_float(c0[k]);
+            t.c[4 + k] = __uint_as_float(c1[k]);
+            t.s[k] = __uint_as_float(s0[k]);
+            t.s[4 + k] = __uint_as_float(s1[k]);
+        }
+    }
+}
+
 // The codec front end for one kept token loaded into t: the fp16 row, for keys the rotary
 // embedding removed at the token's position, then the Hadamard butterflies. x = group_sign(g)
 // times the unnormalised rotated row.
@@ -358,9 +390,19 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
     const int g = lane_group(lane & 15), q = wave * 4 + (lane >> 4);
     const int n_keep = a.n_keep;
     const size_t chain = (size_t)lc * a.H + h;
-    const uint16_t *X = (IS_KEY ? a.K : a.V) +
-                        ((size_t)(a.layer_begin + lc) * a.H + h) * (size_t)a.T * kHeadDim + 8 * g;
-    int8_t *codes = (IS_KEY ? a.codes_k : a.codes_v) + chain * (size_t)n_keep * kHeadDim + 8 * g;
+    ChainBuf b;
+    b.x = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(IS_KEY ? a.K : a.V) +
+            ((size_t)(a.layer_begin + lc) * a.H + h) * (size_t)a.T * kHeadDim,
+        0, a.T * 256, kBufWord3);
+    b.cos = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.rope_cos), 0, a.T * 256,
+                                              kBufWord3);
+    b.sin = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a.rope_sin), 0, a.T * 256,
+                                              kBufWord3);
+    b.codes = __builtin_amdgcn_make_buffer_rsrc(
+        (IS_KEY ? a.codes_k : a.codes_v) + chain * (size_t)n_keep * kHeadDim, 0, n_keep * 128,
+        kBufWord3);
+    const uint32_t lane_code = 8 * g;   // this lane's 8 code bytes of a 128-byte row
     const int t0 = tile * kCodecTile;
     const float rho = IS_KEY ? a.rho_k : a.rho_v;
     const float rho_inv = IS_KEY ? a.rho_inv_k : a.rho_inv_v;
@@ -383,7 +425,7 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
         if (t0 > 0) {
             uint32_t s16;
             TokenIn t;
-            load_token<IS_KEY>(a.rope_cos, a.rope_sin, X, s_pos[-1], g, t);
+            load_token_buf<IS_KEY>(b, s_pos[-1], g, t);
             hc = encode_token<IS_KEY>(t, g, rho, rho_inv, s16);
         }
         s_last[0][g] = hc;
@@ -394,21 +436,27 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
         const int j = j0 + i;
         if (j < n_keep) {
             TokenIn t;
-            load_token<IS_KEY>(a.rope_cos, a.rope_sin, X, s_pos[j - t0], g, t);
+            load_token_buf<IS_KEY>(b, s_pos[j - t0], g, t);
             uint32_t s16;
             const uint2 c = encode_token<IS_KEY>(t, g, rho, rho_inv, s16);
             s_sc[(j - t0) * kGroups + g] = (uint16_t)s16;
-            if (i == 0)
+            if (i == 0) {
                 first = c;
-            else
-                store_stream(codes + (size_t)j * kHeadDim, delta_code(c, prev));
+            } else {
+                const uint2 d = delta_code(c, prev);
+                __builtin_amdgcn_raw_buffer_store_b64((u32x2){d.x, d.y}, b.codes,
+                                                      (uint32_t)j * 128 + lane_code, 0, kBufNt);
+            }
             prev = c;
         }
     }
     s_last[q + 1][g] = prev;
     __syncthreads();
-    if (j0 < n_keep)
-        store_stream(codes + (size_t)j0 * kHeadDim, delta_code(first, s_last[q][g]));
+    if (j0 < n_keep) {
+        const uint2 d = delta_code(first, s_last[q][g]);
+        __builtin_amdgcn_raw_buffer_store_b64((u32x2){d.x, d.y}, b.codes,
+                                              (uint32_t)j0 * 128 + lane_code, 0, kBufNt);
+    }
     // the tile's scales: 32 bytes per token, written as 16-byte chunks past the caches
     const int nt = min(kCodecTile, n_keep - t0);
     uint4 *sc = reinterpret_cast<uint4 *>((IS_KEY ? a.scales_k : a.scales_v) +

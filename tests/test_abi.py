@@ -65,6 +65,7 @@ def test_keep_count_edges(T, W, e):
     ("window", -1, nq.NQ_ERR_INVALID_ARG), ("evict_permille", 1001, nq.NQ_ERR_INVALID_ARG),
     ("layer_end", 2, nq.NQ_ERR_INVALID_ARG), ("layer_begin", 1, nq.NQ_ERR_INVALID_ARG),
     ("rope_base", 1.0, nq.NQ_ERR_INVALID_ARG), ("rope_base", float("nan"), nq.NQ_ERR_INVALID_ARG),
+    ("tokens", 1 << 23, nq.NQ_ERR_UNSUPPORTED),   # row byte offsets past 2^31
 ])
 def test_invalid_params_rejected(field, value, status):
     p = params(kvsynth.workload(0))
@@ -211,3 +212,9 @@ def test_static_decode_rejects_oversize_before_launch():
     # nothing to decode: accepted without a launch
     empty = nq.make_params(1, 2, 0, 8, 600, 3, 2, 1e4)
     nq.nq_decode_static(empty, *([None] * 9), nq.NQ_OUT_F16, stream=0)
+
+
+def test_largest_supported_token_count():
+    p = params(kvsynth.workload(0))
+    p.tokens = (1 << 23) - 1
+    assert nq.nq_check_params(p) == nq.NQ_OK
