@@ -200,12 +200,16 @@ def summarize_counters(args):
     import csv
     from collections import defaultdict
     vals = defaultdict(lambda: defaultdict(list))
+    clock = defaultdict(list)   # GHz: GRBM busy cycles of one XCD over the dispatch's duration
     d = args.summarize_counters[0]
     for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
         if "nq::" not in r["Kernel_Name"]:
             continue
         name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("nq::", "").strip()
         vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and dur > 0:
+            clock[name].append(float(r["Counter_Value"]) / 8 / dur)
     cols = [("SQ_WAVES", "waves", 1.0, "{:.0f}"), ("SQ_INSTS_VALU", "VALU instr (M)", 1e-6, "{:.1f}"),
             ("SQ_INSTS_VMEM_RD", "VMEM rd instr (M)", 1e-6, "{:.2f}"),
             ("SQ_INSTS_VMEM_WR", "VMEM wr instr (M)", 1e-6, "{:.2f}"),
@@ -218,16 +222,20 @@ def summarize_counters(args):
              "kernel. `VALU ms (4 cyc)` = SQ_INSTS_VALU x 4 cycles / (1024 SIMDs x 2.4 GHz): "
              "the time if every VALU instruction took the 4 issue cycles of a wave64 instruction "
              "on a 16-lane SIMD (plain fp32 add/mul, integer and bitwise ops issue in about half "
-             "that on this chip, so this bounds the VALU time from above).", "",
+             "that on this chip, so this bounds the VALU time from above). `clock GHz` = "
+             "GRBM_GUI_ACTIVE / 8 XCDs / the dispatch's duration: the average shader clock "
+             "while the kernel ran (2.4 GHz nominal; meaningful for dispatches longer than "
+             "~50 us).", "",
              "Command (from /tmp with TMPDIR=/tmp; `$REPO` is the repository root):", "", "```",
              args.pmc_command or "(not recorded)", "```", "",
-             "| kernel | " + " | ".join(c[1] for c in cols) + " | VALU ms (4 cyc) |",
-             "|---|" + "---|" * (len(cols) + 1)]
+             "| kernel | " + " | ".join(c[1] for c in cols) + " | VALU ms (4 cyc) | clock GHz |",
+             "|---|" + "---|" * (len(cols) + 2)]
     for k in sorted(vals):
         m = {c: sum(v) / len(v) for c, v in vals[k].items()}
         cells = [fmt.format(m[c] * sc) if c in m else "" for c, _, sc, fmt in cols]
         valu_ms = m.get("SQ_INSTS_VALU", 0.0) * 4 / (1024 * 2.4e9) * 1e3
-        lines.append(f"| {k} | " + " | ".join(cells) + f" | {valu_ms:.3f} |")
+        ghz = f"{sum(clock[k]) / len(clock[k]):.2f}" if clock[k] else ""
+        lines.append(f"| {k} | " + " | ".join(cells) + f" | {valu_ms:.3f} | {ghz} |")
     lines += ["", f"Kernel sources: {kernel_source_hash()}", ""]
     out = os.path.join(ROOT, "profiles", f"counters_{name}.md")
     open(out, "w").write("\n".join(lines))

@@ -126,6 +126,27 @@ __device__ __forceinline__ void hadamard_butterflies(float x[8], int g)
     hadamard_cross_lane(x, g);
 }
 
+// x[k] += sg * u[k] of the partner lane g ^ 8 (row_ror:8), rounded once: the cross term of a
+// RoPE pair (i, i + 64), whose two lanes hold the same (C, S) so that each lane's own product
+// u = x * S is the one its partner needs. One v_fmac_f32_dpp per value (written out: the
+// compiler splits a DPP move from the multiply-add); s_nop 1 as in hadamard_cross_lane.
+__device__ __forceinline__ void rope_cross(float x[8], const float u[8], float sg)
+{
+    asm("s_nop 1\n"
+        "v_fmac_f32_dpp %0, %8, %16 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %1, %9, %16 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %2, %10, %16 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %3, %11, %16 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %4, %12, %16 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %5, %13, %16 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %6, %14, %16 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        "v_fmac_f32_dpp %7, %15, %16 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n"
+        : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),
+          "+v"(x[7])
+        : "v"(u[0]), "v"(u[1]), "v"(u[2]), "v"(u[3]), "v"(u[4]), "v"(u[5]), "v"(u[6]),
+          "v"(u[7]), "v"(sg));
+}
+
 // Nearest E8 point of u (8 floats); returns the codes c = 2y as bytes c + 64 in two dwords.
 // E8 = D8 u (D8 + 1/2) (Conway & Sloane). With f = rint(u), e = u - f, a = |e|:
 //   coset D8:       squared distance sum(a^2), plus (1 - 2 max a) if sum(f) is odd, where the
@@ -296,14 +317,17 @@ __device__ __forceinline__ void front_end(const TokenIn &t, int g, float x[8])
     }
     {
         // RoPE removal, split-half pairs (i, i + 64) = lanes (g, g ^ 8):
-        // x_i = a*C + b*S, x_{i+64} = b*C - a*S with (a, b) = (k_i, k_{i+64}).
+        // x_i = a*C + b*S, x_{i+64} = b*C - a*S with (a, b) = (k_i, k_{i+64}). Both lanes of a
+        // pair hold the same (C, S), so each lane's own product x*S is the one its partner needs:
+        // it is formed in place and crosses over inside the final multiply-add.
         const float sg = g >= 8 ? -1.0f : 1.0f;
+        float u[8];
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-            const float t1 = x[k] * t.c[k];
-            const float t2 = lane_xor8(x[k]) * t.s[k];
-            x[k] = __builtin_fmaf(sg, t2, t1);        // t1 +- t2, rounded once
+            u[k] = x[k] * t.s[k];   // the partner's t2
+            x[k] = x[k] * t.c[k];   // t1
         }
+        rope_cross(x, u, sg);       // t1 +- t2, rounded once
     }
     hadamard_butterflies(x, g);
 }
@@ -633,8 +657,13 @@ __device__ __forceinline__ uint2 chain_lookback(uint32_t *lb_agg, uint32_t *lb_i
 __device__ __forceinline__ void rope_redo(float x[8], int g, const float cr[8], const float sr[8])
 {
     const float sg = g >= 8 ? -1.0f : 1.0f;
+    float u[8];
 #pragma unroll
-    for (int k = 0; k < 8; k++) x[k] = __builtin_fmaf(sg, lane_xor8(x[k]) * sr[k], x[k] * cr[k]);
+    for (int k = 0; k < 8; k++) {
+        u[k] = x[k] * sr[k];   // the partner's product (both lanes hold the same S)
+        x[k] = x[k] * cr[k];
+    }
+    rope_cross(x, u, sg);
 }
 
 // Reconstructs one token of one chain for this lane's 8 dims: x = group_sign(g) times the
