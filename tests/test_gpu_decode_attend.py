@@ -21,15 +21,18 @@ pytestmark = pytest.mark.gpu
 
 FUSED_TOL = 1e-6
 
-# (tokens, window, evict_permille, G, layers, protect_boundary): several 192-token tiles with a
-# ragged tail, a single partial tile, a last tile holding one token, a one-token cache, and a
-# protected-boundary layer range (layer 1 of 3 compressed)
+# (tokens, window, evict_permille, G, layers, protect_boundary, bits_k, bits_v): several
+# 192-token tiles with a ragged tail, a single partial tile, a last tile holding one token, a
+# one-token cache, a protected-boundary layer range (layer 1 of 3 compressed), and the widest
+# codes (4-bit budgets, |c| up to 15) and the narrowest (2-bit)
 CASES = [
-    (2048, 128, 600, 4, 2, 0),
-    (300, 64, 600, 1, 1, 0),
-    (193, 16, 0, 2, 1, 0),
-    (1, 4, 600, 8, 1, 0),
-    (1000, 32, 800, 8, 3, 1),
+    (2048, 128, 600, 4, 2, 0, 3, 2),
+    (300, 64, 600, 1, 1, 0, 3, 2),
+    (193, 16, 0, 2, 1, 0, 3, 2),
+    (1, 4, 600, 8, 1, 0, 3, 2),
+    (1000, 32, 800, 8, 3, 1, 3, 2),
+    (1500, 64, 500, 4, 1, 0, 4, 4),
+    (700, 32, 300, 2, 1, 0, 2, 2),
 ]
 
 
@@ -43,17 +46,18 @@ def oracle_layers(w, T, layers):
     return encs, Ct, St
 
 
-@pytest.mark.parametrize("T,W,e,G,L,pb", CASES)
-def test_decode_attend_on_oracle_cache(T, W, e, G, L, pb):
+@pytest.mark.parametrize("T,W,e,G,L,pb,bk,bv", CASES)
+def test_decode_attend_on_oracle_cache(T, W, e, G, L, pb, bk, bv):
     w = kvsynth.workload(0).with_(tokens=T, window=W, evict_permille=e, layers=L,
-                                  protect_boundary=pb)
+                                  protect_boundary=pb, bits_k=bk, bits_v=bv)
     lb, le = w.layer_begin, w.layer_end
     H = w.kv_heads
     encs, Ct, St = oracle_layers(w, T, range(lb, le))
     p = nq.make_params(L, H, T, W, e, w.bits_k, w.bits_v, w.rope_base, lb, le)
     n = nq.nq_keep_count(p)
     assert all(enc["positions"].size == n for enc in encs)
-    say(f"[decode-attend] T={T} W={W} e={e} G={G} layers [{lb},{le}) of {L}: n_keep={n}")
+    say(f"[decode-attend] T={T} W={W} e={e} G={G} K{bk}V{bv} layers [{lb},{le}) of {L}: "
+        f"n_keep={n}")
     dev = "cuda"
     t = lambda a: torch.from_numpy(np.ascontiguousarray(np.stack(a))).to(dev)
     ck = t([enc["codes_k"] for enc in encs])
