@@ -54,74 +54,6 @@ struct FusedShared {
     } u;
 };
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// One transpose-reduce level across lane partners l ^ m (DPP control CTRL): lanes whose
-// selecting bit is clear keep a + a(partner), the others b + b(partner).
-template <int CTRL>
-__device__ __forceinline__ float tr_level(float a, float b, bool hi)
-{
-    return (hi ? b : a) + dpp_f<CTRL>(hi ? a : b);
-}
-
-// Sums of G per-lane values d[0..G) over the 16 lanes of a row. Transpose-reduce: the levels
-// run over lane partners l ^ 8, l ^ 7, l ^ 2, l ^ 1 (row_ror:8, row_half_mirror, quad_perm);
-// while more than one value is live, each level halves them, keeping in every lane the half
-// picked by one bit of l (bits 3, 2, 1), so all levels together cost G - 1 + log2(16 / G)
-// adds instead of 4 G. Returns the sum of value row_sum_index<G>(l) for this lane l.
-template <int G>
-__device__ __forceinline__ float row_sums(const float (&d)[G], int l)
-{
-    constexpr int kRor8 = kDppRor8, kHm = 0x141, kX2 = 0x4E, kX1 = 0xB1;
-    const bool b3 = l & 8, b2 = l & 4, b1 = l & 2;
-    if constexpr (G == 1) {
-        float v = d[0] + dpp_f<kRor8>(d[0]);
-        v += dpp_f<kHm>(v);
-        v += dpp_f<kX2>(v);
-        return v + dpp_f<kX1>(v);
-    } else if constexpr (G == 2) {
-        float v = tr_level<kRor8>(d[0], d[1], b3);
-        v += dpp_f<kHm>(v);
-        v += dpp_f<kX2>(v);
-        return v + dpp_f<kX1>(v);
-    } else if constexpr (G == 4) {
-        const float v01 = tr_level<kRor8>(d[0], d[1], b3);
-        const float v23 = tr_level<kRor8>(d[2], d[3], b3);
-        float v = tr_level<kHm>(v01, v23, b2);
-        v += dpp_f<kX2>(v);
-        return v + dpp_f<kX1>(v);
-    } else {
-        static_assert(G == 8, "G in {1, 2, 4, 8}");
-        const float v01 = tr_level<kRor8>(d[0], d[1], b3);
-        const float v23 = tr_level<kRor8>(d[2], d[3], b3);
-        const float v45 = tr_level<kRor8>(d[4], d[5], b3);
-        const float v67 = tr_level<kRor8>(d[6], d[7], b3);
-        const float v03 = tr_level<kHm>(v01, v23, b2);
-        const float v47 = tr_level<kHm>(v45, v67, b2);
-        const float v = tr_level<kX2>(v03, v47, b1);
-        return v + dpp_f<kX1>(v);
-    }
-}
-
-// which value row_sums<G> leaves in lane l (0..15), and whether lane l is the one that
-// reports it (one lane per value)
-template <int G>
-__device__ __forceinline__ int row_sum_index(int l)
-{
-    return (G >= 2 ? (l >> 3) & 1 : 0) | (G >= 4 ? ((l >> 2) & 1) << 1 : 0) |
-           (G >= 8 ? ((l >> 1) & 1) << 2 : 0);
-}
-
-template <int G>
-__device__ __forceinline__ bool row_sum_reporter(int l)
-{
-    return (l & (G == 1 ? 15 : G == 2 ? 7 : G == 4 ? 3 : 1)) == 0;
-}
-
 __device__ __forceinline__ void load_f32x4(const float *__restrict__ p, float x[4])
 {
     const float4 v = *reinterpret_cast<const float4 *>(p);

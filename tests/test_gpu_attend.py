@@ -43,3 +43,31 @@ def test_attend_on_oracle_cache(G, n):
     err = np.abs(got - ref).max() / vmax
     say(f"[attend] G={G} n={n}: max err / max|v| = {err:.3g}")
     assert err <= 1e-5
+
+
+def test_attend_multi_tile_chunks():
+    """Chunks of several 256-token tiles with a ragged last one (8 layers x 2 kv heads x 70000
+    tokens: 128 chunks of 547 tokens per head), so the per-tile rescale of the running softmax
+    runs; the fp16 K/V are the synthetic caches themselves."""
+    G, L, H, n = 4, 8, 2, 70000
+    w = kvsynth.workload(0).with_(layers=L, kv_heads=H, tokens=n)
+    p = nq.make_params(L, H, n, w.window, w.evict_permille, w.bits_k, w.bits_v, w.rope_base)
+    K16 = np.empty((L, H, n, 128), np.float16)
+    V16 = np.empty_like(K16)
+    for l in range(L):
+        K16[l], V16[l] = kvsynth.layer_kv(w, l, n)
+    q = np.random.default_rng(4242).standard_normal((L, G * H, 128)).astype(np.float16)
+    dev = "cuda"
+    out = torch.empty((L, G * H, 128), dtype=torch.float32, device=dev)
+    ws = nq.workspace(nq.nq_attend_workspace_bytes(p, G * H, n), dev)
+    nq.nq_attend_decode(p, torch.from_numpy(q).to(dev), G * H, torch.from_numpy(K16).to(dev),
+                        torch.from_numpy(V16).to(dev), n, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for l in range(L):
+        ref = oracle.attend_layer(q[l], K16[l].astype(np.float64), V16[l].astype(np.float64))
+        vmax = np.abs(V16[l].astype(np.float64)).max(axis=(1, 2)).repeat(G)
+        worst = max(worst, float((np.abs(got[l] - ref).max(axis=1) / vmax).max()))
+    say(f"[attend] multi-tile chunks G={G} n={n}: max err / max|v| = {worst:.3g}")
+    assert worst <= 1e-5
