@@ -722,7 +722,7 @@ def decode_step(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for "
               f"--gpus {args.gpus}). The hot path shards by layer with no communication; run "
               f"with --gpus 1.", file=sys.stderr)
         sys.exit(2)

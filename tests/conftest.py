@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) where no GPU is visible, so `-m "not gpu"` and a bare
-    # run on a CPU-only machine both pass; on the GPU machine they run.
+    # run on a CPU-only machine both pass; on a machine with the GPU they run.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
