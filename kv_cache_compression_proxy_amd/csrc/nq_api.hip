@@ -75,6 +75,14 @@ nq_status launched(const char *fn)
     return NQ_ERR_HIP;
 }
 
+// Clears n words (16-byte aligned) and, when ticket is not null, the ticket words, with a
+// kernel (no memset node in a captured graph).
+void launch_reset(uint32_t *words, int64_t n, uint32_t *ticket, hipStream_t s)
+{
+    hipLaunchKernelGGL(nq::k_decode_reset, dim3((uint32_t)((nq::reset_threads(n) + 255) / 256)),
+                       dim3(256), 0, s, words, n, ticket);
+}
+
 struct ScoreWs {
     double *qbar, *scores;
     size_t bytes;
@@ -569,8 +577,7 @@ static nq_status decode_launch(const nq_params *p, const int8_t *codes_k, const 
     hipStream_t s = as_stream(stream);
     clear_error();
     const int64_t words = (int64_t)(w.incl - w.agg) + (int64_t)w.tiles * 64;
-    hipLaunchKernelGGL(nq::k_decode_reset, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0, s,
-                       w.agg, words, w.ticket);
+    launch_reset(w.agg, words, w.ticket, s);
     hipLaunchKernelGGL(nq::k_decode, dim3((uint32_t)w.tiles), dim3(nq::kCodecThreads), 0, s, a);
     return launched(fn);
 }
@@ -637,8 +644,7 @@ nq_status nq_decode_attend(const nq_params *p, const int8_t *codes_k, const int8
     if (n == 0) {   // nothing to attend to: zeros, written by a kernel (no memset node)
         const int64_t words = (int64_t)Lc * q_heads * 128;
         clear_error();
-        hipLaunchKernelGGL(nq::k_decode_reset, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0,
-                           s, (uint32_t *)out, words, nullptr);
+        launch_reset((uint32_t *)out, words, nullptr, s);
         return launched("nq_decode_attend");
     }
     const void *ptrs16[] = {codes_k, codes_v, rope_cos, rope_sin};
@@ -671,8 +677,7 @@ nq_status nq_decode_attend(const nq_params *p, const int8_t *codes_k, const int8
     a.tiles = w.tiles;
     clear_error();
     const int64_t words = (int64_t)(w.incl - w.agg) + (int64_t)w.pairs * w.tiles * 2 * 64;
-    hipLaunchKernelGGL(nq::k_decode_reset, dim3((uint32_t)((words + 255) / 256)), dim3(256), 0, s,
-                       w.agg, words, w.ticket);
+    launch_reset(w.agg, words, w.ticket, s);
     const dim3 grid((uint32_t)((int64_t)w.pairs * w.tiles)), blk(nq::kCodecThreads);
     const dim3 mgrid((uint32_t)(Lc * q_heads));
     switch (G) {

@@ -536,12 +536,21 @@ constexpr int kTicketErr = 1;
 
 // Zeroes n words and, when ticket is not null, the kTicketWords ticket words (a launch of at
 // least kTicketWords threads).
+// words must be 16-byte aligned: each thread clears 4 words with one 16-byte store (the last
+// one clears what is left of n word by word).
 __global__ void k_decode_reset(uint32_t *words, int64_t n, uint32_t *ticket)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) words[i] = 0u;
+    const int64_t w = 4 * i;
+    if (w + 4 <= n)
+        *reinterpret_cast<uint4 *>(words + w) = make_uint4(0u, 0u, 0u, 0u);
+    else
+        for (int64_t k = w; k < n; k++) words[k] = 0u;
     if (ticket && i < kTicketWords) ticket[i] = 0u;
 }
+
+// threads of a k_decode_reset launch for n words (and the ticket words)
+inline int64_t reset_threads(int64_t n) { return (n + 3) / 4 > kTicketWords ? (n + 3) / 4 : kTicketWords; }
 
 // This block's ticket, taken by one thread. Tickets come from m counters, m the largest power
 // of two <= kTicketClasses that divides `chains`; block b draws from counter b mod m, which
