@@ -60,6 +60,13 @@ def parse():
                          "--stats run's kernel_stats.csv (the command given by --pmc-command) "
                          "and exit")
     ap.add_argument("--title", default="", help="title line of a --summarize-trace summary")
+    ap.add_argument("--timed-steps", type=int, default=0,
+                    help="with --summarize-trace: also average each kernel over its last N "
+                         "dispatches (the profiled run's timed steps), from the kernel_trace.csv "
+                         "beside the stats CSV")
+    ap.add_argument("--bench-log", default="",
+                    help="with --summarize-trace: the profiled run's output; its JSON line's "
+                         "roofline kernel and event-timed launch average are quoted")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("PMC_DIR", "NAME"),
                     help="write profiles/counters_<NAME>.md from a rocprofv3 --pmc run of SQ "
                          "instruction counters (the command given by --pmc-command) and exit")
@@ -172,23 +179,55 @@ def summarize_pmc(args, w, decode_step: bool = False):
 
 def summarize_trace(args):
     """rocprofv3 kernel stats CSV -> profiles/kernel_trace_<name>.md (per-kernel calls and
-    durations)."""
+    durations; with --timed-steps N also each kernel's average over its last N dispatches, the
+    steps the profiled run timed, next to the run's own event-timed figure from --bench-log)."""
     import csv
+    from collections import defaultdict
     rows = list(csv.DictReader(open(args.summarize_trace[0])))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     name = args.summarize_trace[1]
+    timed = {}
+    if args.timed_steps > 0:
+        durs = defaultdict(list)
+        trace = os.path.join(os.path.dirname(args.summarize_trace[0]), "run_kernel_trace.csv")
+        for r in sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"])):
+            durs[r["Kernel_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        for k, v in durs.items():
+            if len(v) >= args.timed_steps:
+                last = v[-args.timed_steps:]
+                timed[k] = (sum(last) / len(last), min(last), max(last))
+    head = "| kernel | calls | avg us | min us | max us | share % |"
+    rule = "|---|---|---|---|---|---|"
+    if timed:
+        head += f" avg us, last {args.timed_steps} |"
+        rule += "---|"
     lines = [f"# rocprofv3 kernel stats: {args.title or name}", "",
              "Command (from /tmp, with TMPDIR=/tmp; `$REPO` is the repository root):", "", "```",
-             args.pmc_command or "(not recorded)", "```", "",
-             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+             args.pmc_command or "(not recorded)", "```", "", head, rule]
     for r in rows:
-        lines.append(f"| {r['Name'][:120]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                     f"{float(r['Percentage']):.2f} |")
+        line = (f"| {r['Name'][:120]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                f"{float(r['Percentage']):.2f} |")
+        if timed:
+            t = timed.get(r["Name"])
+            line += f" {t[0]:.2f} |" if t else " |"
+        lines.append(line)
     lines += ["", "Kernels outside `nq::` belong to bench.py itself (torch's fills and copies of "
               "inputs; in a headline run also the 1 GiB device copy timed as the achievable "
-              "line); the shares include them.", "",
-              f"Kernel sources: {kernel_source_hash()}", ""]
+              "line); the shares include them."]
+    if timed:
+        lines += ["", f"`avg us, last {args.timed_steps}`: each kernel's average over its last "
+                  f"{args.timed_steps} dispatches in the per-dispatch trace -- the run's timed "
+                  "steps, after its warm-up steps (the first dispatches run while the board's "
+                  "clock settles)."]
+    if args.bench_log:
+        res = [json.loads(ln) for ln in open(args.bench_log) if ln.startswith("{")]
+        if res and "roofline" in res[-1]:
+            rf = res[-1]["roofline"]
+            lines += ["", f"The profiled run's own line: roofline kernel `{rf.get('kernel')}`, "
+                      f"event-timed average {rf.get('avg_launch_ms')} ms per launch over its "
+                      f"{res[-1].get('steps')} timed steps."]
+    lines += ["", f"Kernel sources: {kernel_source_hash()}", ""]
     out = os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md")
     open(out, "w").write("\n".join(lines))
     log(f"[bench] wrote {out}")
