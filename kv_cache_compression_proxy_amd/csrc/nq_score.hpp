@@ -107,6 +107,7 @@ __global__ __launch_bounds__(256) void k_scores(const uint16_t *__restrict__ K,
 // the window, the candidates above that key and the lowest-positioned ones equal to it.
 constexpr int kSelThreads = 1024;
 constexpr int kHistCopies = 16;   // LDS histogram copies of the radix passes (lane mod 16)
+constexpr int kSelCompact = 4096; // bucket size up to which k_select_mem gathers it into LDS
 
 __device__ __forceinline__ uint64_t order_key(double d)
 {
@@ -148,6 +149,7 @@ struct SelectShared {
     uint64_t wave_min[kSelThreads / 64], wave_max[kSelThreads / 64];
     uint64_t prefix, mask;   // bits of the m-th best key resolved so far
     int krem;                // rank of that key among the keys matching prefix/mask
+    uint32_t bucket;         // number of keys matching prefix/mask
     int all;                 // the whole matching bucket is kept
     int bits;                // bits left to resolve
 };
@@ -226,6 +228,7 @@ __device__ __forceinline__ void sel_pick_digit(SelectShared &sh, int shift, uint
                     sh.prefix = prefix | ((uint64_t)dgt << shift);
                     sh.mask = mask | ((uint64_t)dmask << shift);
                     sh.krem = krem - (int)above;
+                    sh.bucket = c[i];
                     if (c[i] == (uint32_t)(krem - (int)above)) sh.all = 1;
                     break;
                 }
@@ -528,6 +531,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
     __shared__ SelectShared sh;
     __shared__ uint32_t s_cnt[kCnt];
     __shared__ uint32_t s_gt[kWords][kSelThreads], s_eq[kWords][kSelThreads];
+    __shared__ uint64_t s_ck[kSelCompact];   // the chosen bucket's keys, once it is small
+    __shared__ uint32_t s_nck;
     const int lc = blockIdx.x;
     const double *s = scores + (size_t)lc * T;
     int32_t *out = positions + (size_t)lc * n_keep;
@@ -561,28 +566,61 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
     }
     __syncthreads();
     if (partial) {
+        // Once the chosen bucket holds at most kSelCompact keys, they are gathered into LDS and
+        // the remaining passes count only them, instead of re-reading every score per pass.
+        bool compact = false;
         for (int top = sh.bits; top > 0; top -= 8) {
             const int shift = top >= 8 ? top - 8 : 0;
             const uint32_t dmask = top >= 8 ? 255u : ((1u << top) - 1u);
             sel_clear_hist(sh);
             const uint64_t prefix = sh.prefix, mask = sh.mask;
-    #pragma unroll 1
-        for (int u0 = 0; u0 < KPT; u0 += kBatch) {
-                double v[kBatch];
-#pragma unroll
-                for (int b = 0; b < kBatch; b++) {
-                    const int t = 1 + tid + (u0 + b) * kSelThreads;
-                    v[b] = t < c_end ? s[t] : 0.0;
+            if (compact) {
+                const int nck = (int)s_nck;
+                for (int i = tid; i < nck; i += kSelThreads) {
+                    const uint64_t k = s_ck[i];
+                    if ((k & mask) == prefix) sel_count(sh, k, shift, dmask);
                 }
+            } else {
+#pragma unroll 1
+                for (int u0 = 0; u0 < KPT; u0 += kBatch) {
+                    double v[kBatch];
 #pragma unroll
-                for (int b = 0; b < kBatch; b++) {
-                    const uint64_t k = order_key(v[b]);
-                    if (1 + tid + (u0 + b) * kSelThreads < c_end && (k & mask) == prefix)
-                        sel_count(sh, k, shift, dmask);
+                    for (int b = 0; b < kBatch; b++) {
+                        const int t = 1 + tid + (u0 + b) * kSelThreads;
+                        v[b] = t < c_end ? s[t] : 0.0;
+                    }
+#pragma unroll
+                    for (int b = 0; b < kBatch; b++) {
+                        const uint64_t k = order_key(v[b]);
+                        if (1 + tid + (u0 + b) * kSelThreads < c_end && (k & mask) == prefix)
+                            sel_count(sh, k, shift, dmask);
+                    }
                 }
             }
             sel_pick_digit(sh, shift, dmask, prefix, mask);
             if (sh.all) break;
+            if (!compact && shift > 0 && sh.bucket <= (uint32_t)kSelCompact) {
+                const uint64_t p2 = sh.prefix, m2 = sh.mask;
+                if (tid == 0) s_nck = 0u;
+                __syncthreads();
+#pragma unroll 1
+                for (int u0 = 0; u0 < KPT; u0 += kBatch) {
+                    double v[kBatch];
+#pragma unroll
+                    for (int b = 0; b < kBatch; b++) {
+                        const int t = 1 + tid + (u0 + b) * kSelThreads;
+                        v[b] = t < c_end ? s[t] : 0.0;
+                    }
+#pragma unroll
+                    for (int b = 0; b < kBatch; b++) {
+                        const uint64_t k = order_key(v[b]);
+                        if (1 + tid + (u0 + b) * kSelThreads < c_end && (k & m2) == p2)
+                            s_ck[atomicAdd(&s_nck, 1u)] = k;
+                    }
+                }
+                __syncthreads();
+                compact = true;
+            }
         }
     }
     const uint64_t prefix = sh.prefix, mask = sh.mask;
