@@ -497,6 +497,9 @@ static nq::CodecArgs codec_args(const nq_params *p, const int32_t *positions,
     a.rho_v = rho_of(p->bits_v);
     a.rho_inv_k = 1.0f / a.rho_k;   // IEEE division on the host: the nearest fp32
     a.rho_inv_v = 1.0f / a.rho_v;
+    // the rest of 1/rho, rounded to fp32 (rho_inv + rho_inv_lo is 1/rho to ~2^-49 relative)
+    a.rho_inv_lo_k = (float)(1.0 / (double)a.rho_k - (double)a.rho_inv_k);
+    a.rho_inv_lo_v = (float)(1.0 / (double)a.rho_v - (double)a.rho_inv_v);
     return a;
 }
 

@@ -37,6 +37,7 @@ struct CodecArgs {
     int32_t dec_tiles_per_chain;   // decode tiles (kDecTile tokens) per chain
     float rho_k, rho_v;
     float rho_inv_k, rho_inv_v;    // fp32 nearest to 1/rho
+    float rho_inv_lo_k, rho_inv_lo_v;   // fp32 nearest to 1/rho - rho_inv
     int32_t out_f32;
 };
 
@@ -334,9 +335,19 @@ __device__ __forceinline__ void front_end(const TokenIn &t, int g, float x[8])
 
 // Encodes one loaded token for this lane's 8 dims. Returns the absolute code bytes (offset
 // +64) and the fp16 scale bits of this lane's group.
+//
+// Both divisions (amax / rho for the scale, xn / s for the lattice input) are a product with a
+// two-part reciprocal h + l of the divisor d, h within an ulp of 1/d and l = (1 - d h) h (the
+// bracket is exact in one fma): a / d is formed as fma(a, h, a * l), one rounded product and
+// one fused multiply-add. h + l is within 2^-45 (relative) of 1/d, and with an 11-bit divisor
+// significand (a binary16 s, rho <= 7) the quotient of any fp32 lies at least 2^-36 (relative)
+// from a midpoint between fp32 neighbours, so the single rounding gives the correctly rounded
+// quotient -- whenever a * l does not underflow, i.e. for every quotient above 2^-100; below,
+// the result is within one ulp of it. Checked on the host: every fp32 significand against
+// every binary16 significand and both candidate values of h, and every fp32 amax for the scale.
 template <bool IS_KEY>
 __device__ __forceinline__ uint2 encode_token(const TokenIn &t, int g, float rho, float rho_inv,
-                                              uint32_t &s16)
+                                              float rho_inv_lo, uint32_t &s16)
 {
     float x[8];
     front_end<IS_KEY>(t, g, x);
@@ -346,12 +357,8 @@ __device__ __forceinline__ uint2 encode_token(const TokenIn &t, int g, float rho
     // the normalised row is x * fp32(1/sqrt(128)); rounding is monotone, so the group's
     // largest normalised magnitude is the rounded product of the largest raw one
     amax = amax * kInvSqrt128;
-    // amax / rho correctly rounded: q = amax * (1/rho), then one remainder correction
-    // (Markstein: with 1/rho rounded to nearest and q within an ulp, the corrected quotient is
-    // the correctly rounded one). amax = 0 gives s = 0.
-    const float q0 = amax * rho_inv;
-    const float rem = __builtin_fmaf(-q0, rho, amax);
-    const float q = __builtin_fmaf(rem, rho_inv, q0);
+    // amax / rho correctly rounded (1/rho in two parts from the host); amax = 0 gives s = 0
+    const float q = __builtin_fmaf(amax, rho_inv, amax * rho_inv_lo);
     // s = the smallest fp16 >= q, saturating at 65504. In the normal fp16 range, rounding q's
     // fp32 bits up at bit 13 gives s's fp32 bits (a mantissa carry moves into the exponent);
     // below 2^-14 (and for q = 0) fp16 steps are 2^-24 apart: s = ceil(q * 2^24) * 2^-24.
@@ -362,25 +369,20 @@ __device__ __forceinline__ uint2 encode_token(const TokenIn &t, int g, float rho
         s16 = (uint32_t)m;
         sb32 = __float_as_uint(m * 0x1p-24f);
     }
-    // u = xn / s correctly rounded, xn = the normalised rotated value (x times the lane sign
-    // and 1/sqrt(128), rounded once): the lattice step sees exactly the oracle's input.
-    // r = 1/s rounded to nearest: v_rcp_f32 is within one ulp, and one Newton step with fused
-    // multiply-adds rounds it correctly for every binary16 s. With r correctly rounded and
-    // q0 = xn * r, the remainder xn - q0 * s is exact in one fma, and q0 + rem * r rounded
-    // once is the correctly rounded quotient (Markstein's division theorem). Both claims are
-    // checked exhaustively over the significands on the host. A zero scale (an all-zero
-    // group) takes r = 0, which keeps u = 0.
+    // u = xn / s, xn = the normalised rotated value (x times the lane sign and 1/sqrt(128),
+    // rounded once), with h from v_rcp_f32 (within one ulp): the lattice step sees the
+    // oracle's u (equal above 2^-100, where a one-ulp step moves no lattice distance by more
+    // than 2^-99). A zero scale (an all-zero group, or one whose a / rho rounds to 0) takes
+    // h = l = 0, which gives u = 0 as the oracle's.
     const float sf = __uint_as_float(sb32);
-    const float r0 = __builtin_amdgcn_rcpf(sf);
-    const float r1 = __builtin_fmaf(__builtin_fmaf(-sf, r0, 1.0f), r0, r0);
-    const float r = s16 ? r1 : 0.0f;
+    const float rh = s16 ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+    const float rl = __builtin_fmaf(-sf, rh, 1.0f) * rh;
     const float cs = kInvSqrt128 * group_sign(g);   // exact: +-fp32(1/sqrt(128))
     float u[8];
 #pragma unroll
     for (int k = 0; k < 8; k++) {
         const float xn = x[k] * cs;
-        const float q0 = xn * r;
-        u[k] = __builtin_fmaf(__builtin_fmaf(-q0, sf, xn), r, q0);
+        u[k] = __builtin_fmaf(xn, rh, xn * rl);
     }
     if (s16 == 0x7bffu) {   // saturated scale: |x / s| may exceed rho
 #pragma unroll
@@ -430,6 +432,7 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
     const int t0 = tile * kCodecTile;
     const float rho = IS_KEY ? a.rho_k : a.rho_v;
     const float rho_inv = IS_KEY ? a.rho_inv_k : a.rho_inv_v;
+    const float rho_inv_lo = IS_KEY ? a.rho_inv_lo_k : a.rho_inv_lo_v;
     const uint2 zero = make_uint2(0x40404040u, 0x40404040u);   // code 0 in offset form
 
     // positions of tokens t0 - 1 .. t0 + kCodecTile - 1 (clamped into the cache) to LDS
@@ -450,7 +453,7 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
             uint32_t s16;
             TokenIn t;
             load_token_buf<IS_KEY>(b, s_pos[-1], g, t);
-            hc = encode_token<IS_KEY>(t, g, rho, rho_inv, s16);
+            hc = encode_token<IS_KEY>(t, g, rho, rho_inv, rho_inv_lo, s16);
         }
         s_last[0][g] = hc;
     }
@@ -462,7 +465,7 @@ __device__ void encode_tile(const CodecArgs &a, int lc, int h, int tile, EncodeS
             TokenIn t;
             load_token_buf<IS_KEY>(b, s_pos[j - t0], g, t);
             uint32_t s16;
-            const uint2 c = encode_token<IS_KEY>(t, g, rho, rho_inv, s16);
+            const uint2 c = encode_token<IS_KEY>(t, g, rho, rho_inv, rho_inv_lo, s16);
             s_sc[(j - t0) * kGroups + g] = (uint16_t)s16;
             if (i == 0) {
                 first = c;

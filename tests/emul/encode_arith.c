@@ -8,17 +8,19 @@
  * integer decisions in fp32 with its own operation sequence. This program shows which of
  * them are exact and bounds the rest:
  *
- *   scale     a/rho as q0 = a * RN(1/rho), q = fma(fma(-q0, rho, a), RN(1/rho), q0):
- *             equal to the correctly rounded a/rho for every fp32 significand of a and
- *             rho in {1, 3, 7}                                           (exhaustive)
+ *   scale     a/rho as fma(a, h, a * l) with h = RN(1/rho), l = RN(1/rho - h): equal to the
+ *             correctly rounded a/rho for every positive fp32 a whose quotient is at least
+ *             2^-100, and zero exactly when it is, for rho in {1, 3, 7}     (exhaustive)
  *   fp16 up   the smallest binary16 >= q by integer rounding of q's bits (and ceil(q * 2^24)
  *             below 2^-14): equal to the oracle's rounding for every positive fp32 q
  *                                                                        (exhaustive)
- *   1/s       one Newton step r = fma(fma(-s, r0, 1), r0, r0) from any r0 within 2 ulps of
- *             1/s gives RN(1/s), for every positive finite binary16 s   (exhaustive)
- *   u         q0 = xn * r, u = fma(fma(-q0, s, xn), r, q0) with r = RN(1/s) equals the
- *             correctly rounded xn / s for every fp32 significand of xn and every binary16
- *             significand of s                                           (exhaustive)
+ *   1/s       h = any fp32 within one ulp of 1/s (what v_rcp_f32 may return) and
+ *             l = fma(-s, h, 1) * h: the fma is exact and h + l is 1/s to 2^-45 relative,
+ *             for every positive finite binary16 s                      (exhaustive)
+ *   u         fma(xn, h, xn * l) equals the correctly rounded xn / s for every fp32
+ *             significand of xn, every binary16 significand of s and both h (exhaustive),
+ *             and, over random exponents, for every quotient of at least 2^-100, with at most
+ *             one ulp of difference below                               (random)
  *   E8        the kernel's decision (rint by a magic add, distance differences in fp32,
  *             arg-max/min on |e| keys whose 3 low bits hold the index) against the oracle's
  *             nearest point: every disagreement must fall inside the oracle's Voronoi
@@ -46,11 +48,12 @@ static uint32_t fbits(float f) { uint32_t b; memcpy(&b, &f, 4); return b; }
 static float bitsf(uint32_t b) { float f; memcpy(&f, &b, 4); return f; }
 
 /* ---- the kernel's sequences, restated -------------------------------------------------- */
-static float k_scale_quotient(float a, float rho, float rho_inv)
+/* rest of 1/rho as the host side computes it */
+static float k_rho_inv_lo(float rho, float rinv) { return (float)(1.0 / (double)rho - (double)rinv); }
+
+static float k_scale_quotient(float a, float rinv, float rinv_lo)
 {
-    float q0 = a * rho_inv;
-    float rem = fmaf(-q0, rho, a);
-    return fmaf(rem, rho_inv, q0);
+    return fmaf(a, rinv, a * rinv_lo);
 }
 
 /* the smallest binary16 >= q (q >= 0), saturating at 65504: fp16 bits */
@@ -63,12 +66,17 @@ static uint32_t k_f16_ceil(float q)
     return s16 & 0xffffu;
 }
 
-static float k_recip(float s, float r0) { return fmaf(fmaf(-s, r0, 1.0f), r0, r0); }
+/* rest of 1/s from h */
+static float k_recip_lo(float s, float h) { return fmaf(-s, h, 1.0f) * h; }
 
-static float k_quotient(float xn, float s, float r)
+static float k_quotient(float xn, float h, float l) { return fmaf(xn, h, xn * l); }
+
+/* the fp32 neighbour of RN(1/s) on the other side of 1/s (above it when 1/s is exact): with
+ * RN(1/s), the values a reciprocal accurate to one ulp may return */
+static float other_recip(float s)
 {
-    float q0 = xn * r;
-    return fmaf(fmaf(-q0, s, xn), r, q0);
+    float r = 1.0f / s;
+    return bitsf(fbits(r) + ((double)r > 1.0 / (double)s ? (uint32_t)-1 : 1u));
 }
 
 /* e8_nearest_code: codes c = 2y */
@@ -110,19 +118,21 @@ static void k_e8(const float u[8], int8_t c[8])
 }
 
 /* ---- exhaustive checks ------------------------------------------------------------------- */
-static long check_scale_quotient(void)
+static long check_scale_quotient(long *cases)
 {
-    long bad = 0;
+    long bad = 0, n = 0;
     const float rhos[3] = {1.0f, 3.0f, 7.0f};
     for (int k = 0; k < 3; k++) {
-        float rho = rhos[k], rinv = 1.0f / rho;
-        /* every significand, in two binades (a / rho lands in both sides of a binade edge) */
-#pragma omp parallel for reduction(+ : bad) schedule(static)
-        for (uint32_t m = 0; m < (1u << 24); m++) {
-            float a = bitsf(0x3f800000u + m);      /* [1, 4) */
-            if (k_scale_quotient(a, rho, rinv) != a / rho) bad++;
+        float rho = rhos[k], rinv = 1.0f / rho, rlo = k_rho_inv_lo(rho, rinv);
+        /* every positive finite fp32 */
+#pragma omp parallel for reduction(+ : bad, n) schedule(static)
+        for (uint32_t b = 1; b < 0x7f800000u; b++) {
+            float a = bitsf(b), want = a / rho, q = k_scale_quotient(a, rinv, rlo);
+            n++;
+            if (want >= 0x1p-100f ? q != want : (q == 0.0f) != (want == 0.0f)) bad++;
         }
     }
+    *cases = n;
     return bad;
 }
 
@@ -141,38 +151,81 @@ static long check_f16_ceil(void)
     return bad;
 }
 
-static long check_recip(long *cases)
+/* every fp32 h within one ulp of 1/s, for every positive finite binary16 s: fma(-s, h, 1)
+ * exact, and the largest |h + l - 1/s| * s */
+static long check_recip(long *cases, double *worst)
 {
     long bad = 0;
     *cases = 0;
-    for (uint32_t h = 1; h < 0x7c00u; h++) {
-        float s = nqo_h2f((uint16_t)h);
-        float want = 1.0f / s;
-        for (int d = -2; d <= 2; d++) {
-            float r0 = bitsf(fbits(want) + (uint32_t)d);
+    *worst = 0.0;
+    for (uint32_t hb = 1; hb < 0x7c00u; hb++) {
+        float s = nqo_h2f((uint16_t)hb);
+        double want = 1.0 / (double)s;
+        for (int d = -1; d <= 1; d++) {
+            float h = bitsf(fbits(1.0f / s) + (uint32_t)d);
+            if (fabs((double)h - want) > ldexp(1.0, ilogb(want) - 23)) continue;
             (*cases)++;
-            if (k_recip(s, r0) != want) bad++;
+            if ((double)fmaf(-s, h, 1.0f) != 1.0 - (double)s * (double)h) bad++;
+            double err = fabs(((double)h + (double)k_recip_lo(s, h)) * (double)s - 1.0);
+            if (err > *worst) *worst = err;
         }
     }
+    if (*worst > 0x1p-45) bad++;
     return bad;
 }
 
-/* every binary16 significand S (s in [1, 2)) against every fp32 significand of xn in [1, 2),
- * the latter with the given stride (1 = exhaustive) */
+/* every binary16 significand S (s in [1, 2)) and both candidate h against every fp32
+ * significand of xn in [1, 2), the latter with the given stride (1 = exhaustive) */
 static long check_quotient(uint32_t stride, long *cases)
 {
     long bad = 0, n = 0;
 #pragma omp parallel for reduction(+ : bad, n) schedule(dynamic)
     for (uint32_t S = 0; S < 1024; S++) {
         float s = 1.0f + (float)S / 1024.0f;
-        float r = 1.0f / s;
-        for (uint32_t m = 0; m < (1u << 23); m += stride) {
-            float xn = bitsf(0x3f800000u + m);
-            n++;
-            if (k_quotient(xn, s, r) != xn / s) bad++;
+        const float hs[2] = {1.0f / s, other_recip(s)};
+        for (int i = 0; i < 2; i++) {
+            float h = hs[i], l = k_recip_lo(s, h);
+            for (uint32_t m = 0; m < (1u << 23); m += stride) {
+                float xn = bitsf(0x3f800000u + m);
+                n++;
+                if (k_quotient(xn, h, l) != xn / s) bad++;
+            }
         }
     }
     *cases = n;
+    return bad;
+}
+
+static uint64_t rng_state;
+static uint64_t next_u64(void);
+
+/* random xn over the whole fp32 range and random binary16 s (quotients from ~2^-165 up to a
+ * few units): equal to xn / s at or above 2^-100, within one ulp below */
+static long check_quotient_range(long n, long *below, long *below_differ)
+{
+    long bad = 0;
+    *below = *below_differ = 0;
+    for (long k = 0; k < n; k++) {
+        uint32_t hb = 1u + (uint32_t)(next_u64() % 0x7bffu);
+        float s = nqo_h2f((uint16_t)hb);
+        float h = (next_u64() & 1) ? 1.0f / s : other_recip(s), l = k_recip_lo(s, h);
+        /* |xn| up to 8 s, down to the smallest subnormal */
+        int e = -150 + (int)(next_u64() % 154);
+        float xn = (float)ldexp(1.0 + (double)(next_u64() >> 11) * 0x1p-53, e) * s;
+        if (next_u64() & 1) xn = -xn;
+        if (!(fabsf(xn) <= 8.0f * s)) continue;
+        float want = xn / s, got = k_quotient(xn, h, l);
+        if (fabsf(want) >= 0x1p-100f) {
+            if (got != want) bad++;
+        } else {
+            (*below)++;
+            if (got != want) {
+                (*below_differ)++;
+                int32_t d = (int32_t)fbits(got) - (int32_t)fbits(want);
+                if (d > 1 || d < -1) bad++;
+            }
+        }
+    }
     return bad;
 }
 
@@ -204,7 +257,7 @@ typedef struct {
  * oracle's quantize_row on the same group */
 static void one_group(const float x8[8], const float *raw8, int bits, e8_stats *st)
 {
-    float rho = (float)((1 << (bits - 1)) - 1), rinv = 1.0f / rho;
+    float rho = (float)((1 << (bits - 1)) - 1), rinv = 1.0f / rho, rlo = k_rho_inv_lo(rho, rinv);
     float row[128];
     memset(row, 0, sizeof(row));
     memcpy(row, x8, sizeof(float) * 8);
@@ -214,13 +267,15 @@ static void one_group(const float x8[8], const float *raw8, int bits, e8_stats *
     nqo_quantize_row(row, bits, s16o, co, fl);
     float a = 0.0f;
     for (int i = 0; i < 8; i++) a = fmaxf(a, fabsf(x8[i]));
-    uint32_t s16 = k_f16_ceil(k_scale_quotient(a, rho, rinv));
+    uint32_t s16 = k_f16_ceil(k_scale_quotient(a, rinv, rlo));
     st->groups++;
     if (s16 != s16o[0]) { st->differ++; st->outside_band++; return; }   /* proven equal */
     if (s16 == 0) return;
-    float s = nqo_h2f((uint16_t)s16), r = k_recip(s, 1.0f / s), u[8], uo[8];
+    /* either reciprocal the kernel's v_rcp_f32 may return */
+    float s = nqo_h2f((uint16_t)s16), u[8], uo[8];
+    float h = (st->groups & 1) ? 1.0f / s : other_recip(s), l = k_recip_lo(s, h);
     for (int i = 0; i < 8; i++) {
-        u[i] = k_quotient(x8[i], s, r);
+        u[i] = k_quotient(x8[i], h, l);
         if (s16 == 0x7bffu) u[i] = fminf(fmaxf(u[i], -rho), rho);
     }
     float umax = nqo_group_u(x8, (uint16_t)s16, bits, uo);
@@ -366,17 +421,23 @@ int main(int argc, char **argv)
     int ok = 1;
     long bad, cases;
 
-    bad = check_scale_quotient();
-    printf("scale_quotient cases=%ld bad=%ld\n", 3L << 24, bad);
+    bad = check_scale_quotient(&cases);
+    printf("scale_quotient cases=%ld bad=%ld\n", cases, bad);
     ok &= bad == 0;
     bad = check_f16_ceil();
     printf("f16_ceil cases=%ld bad=%ld\n", (long)0x477fe001u + 4, bad);
     ok &= bad == 0;
-    bad = check_recip(&cases);
-    printf("reciprocal cases=%ld bad=%ld\n", cases, bad);
+    double worst;
+    bad = check_recip(&cases, &worst);
+    printf("reciprocal cases=%ld bad=%ld worst_rel_err=%.3g\n", cases, bad, worst);
     ok &= bad == 0;
     bad = check_quotient(stride, &cases);
     printf("quotient cases=%ld bad=%ld stride=%u\n", cases, bad, stride);
+    ok &= bad == 0;
+    long below, below_differ;
+    bad = check_quotient_range(n_random * 4, &below, &below_differ);
+    printf("quotient_range cases=%ld bad=%ld below_2^-100=%ld of_which_differ=%ld\n",
+           n_random * 4, bad, below, below_differ);
     ok &= bad == 0;
     for (int bits = 2; bits <= 4; bits++) {
         e8_stats st;

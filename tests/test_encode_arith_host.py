@@ -1,11 +1,16 @@
 """The GPU encode's fp32 arithmetic, emulated on the host (tests/emul/encode_arith.c) and checked
 against the oracle. The kernel's lattice codes may differ from the oracle's only inside the
 near-tie bands; this test shows why:
-- its group scale a/rho (a corrected product with 1/rho) and the round-up to binary16 (integer
-  rounding of the fp32 bits) equal the oracle's for every input (exhaustive);
-- its u = x/s (a Newton-corrected v_rcp_f32 and a Markstein-corrected product) equals the
-  correctly rounded quotient for every binary16 scale and every fp32 significand (exhaustive:
-  8.6e9 pairs), so the lattice step sees exactly the oracle's u;
+- both of its divisions are one product with a two-part reciprocal h + l of the divisor and
+  one fused multiply-add; h + l is 1/d to 2^-45 for every binary16 divisor and every h that a
+  reciprocal accurate to one ulp may return (exhaustive);
+- its group scale a/rho and the round-up to binary16 (integer rounding of the fp32 bits) equal
+  the oracle's for every positive fp32 a (exhaustive);
+- its u = x/s equals the correctly rounded quotient for every binary16 significand, both
+  candidate reciprocals and every fp32 significand (exhaustive: 1.7e10 cases), and over
+  random exponents for every quotient of at least 2^-100 (below, within one ulp, which moves
+  no lattice distance by more than 2^-99, far inside the near-tie band): the lattice step sees
+  the oracle's u;
 - its E8 decision in fp32 (magic-number rounding, distance differences, arg-max/min keys
   carrying the index in their low bits) agrees with the oracle's exact nearest point except
   inside the Voronoi near-tie band, on millions of random groups and on groups built on and
@@ -50,10 +55,12 @@ def test_encode_arithmetic_matches_the_oracle(harness):
     print(r.stdout)
     lines = {ln.split()[0] + (ln.split()[1] if ln.startswith("e8") else ""): ln
              for ln in r.stdout.splitlines() if ln.strip()}
-    for name in ("scale_quotient", "f16_ceil", "reciprocal", "quotient"):
+    for name in ("scale_quotient", "f16_ceil", "reciprocal", "quotient", "quotient_range"):
         assert re.search(r"\bbad=0\b", lines[name]), lines[name]
     assert "stride=1" in lines["quotient"]                       # exhaustive
-    assert int(re.search(r"cases=(\d+)", lines["quotient"]).group(1)) == 1024 << 23
+    assert int(re.search(r"cases=(\d+)", lines["quotient"]).group(1)) == 2 * (1024 << 23)
+    # every positive finite fp32 for each of the three radii
+    assert int(re.search(r"cases=(\d+)", lines["scale_quotient"]).group(1)) == 3 * (0x7f800000 - 1)
     for bits in (2, 3, 4):
         ln = lines[f"e8bits={bits}"]
         kv = dict(kv.split("=") for kv in ln.split()[1:])
