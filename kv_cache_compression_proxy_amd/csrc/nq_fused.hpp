@@ -54,18 +54,13 @@ struct FusedShared {
     } u;
 };
 
-__device__ __forceinline__ void load_f32x4(const float *__restrict__ p, float x[4])
-{
-    const float4 v = *reinterpret_cast<const float4 *>(p);
-    x[0] = v.x, x[1] = v.y, x[2] = v.z, x[3] = v.w;
-}
-
 // One key row in the fused kernel's key layout: lane g holds dims 4g + m (x[m]) and
 // 64 + 4g + m (x[4 + m]), m = 0..3, so both members of each RoPE pair (i, i + 64) sit in one
 // lane. code: the running code bytes of those dims (offset form c + 64; .x the low dims, .y the
-// high ones); hs_lo, hs_hi: (s / 2) / sqrt(128) for their groups g / 2 and 8 + g / 2; (cr, sr):
-// the rotary table row of the token's position at dims 4g..4g+3. Returns x = group_sign(g)
-// times the reconstructed key, K = RoPE(H y) with H the normalised Hadamard transform.
+// high ones); s_lo, s_hi: the fp16 scales of their groups g / 2 and 8 + g / 2 in the low
+// halves; (cr, sr): the rotary table row of the token's position at dims 4g..4g+3. Returns
+// x = group_sign(g) * 2 sqrt(128) times the reconstructed key K = RoPE(H y), H the normalised
+// Hadamard transform: the constant factor is left to the caller (the queries carry it).
 //
 // The Hadamard stages commute, so they run in the order this layout makes cheap: h = 1, 2 on
 // the integer codes in packed fp16 (exact, as in decode_row), the scale, h = 4, 8, 16, 32 across
@@ -73,7 +68,7 @@ __device__ __forceinline__ void load_f32x4(const float *__restrict__ p, float x[
 // h = 64 inside the lane fused with the rotation: with (a, b) = the pair before stage 64,
 //   k_i      = (a + b) C - (a - b) S = a (C - S) + b (C + S),
 //   k_{i+64} = (a - b) C + (a + b) S = a (C + S) - b (C - S).
-__device__ __forceinline__ void decode_key_split(int g, uint2 code, float hs_lo, float hs_hi,
+__device__ __forceinline__ void decode_key_split(int g, uint2 code, uint32_t s_lo, uint32_t s_hi,
                                                  const float cr[4], const float sr[4], float x[8])
 {
     uint32_t q0 = __builtin_amdgcn_perm(0x64646464u, code.x, 0x04010400u);   // (c0, c1)
@@ -99,18 +94,18 @@ __device__ __forceinline__ void decode_key_split(int g, uint2 code, float hs_lo,
         "v_pk_add_f16 %3, %6, %7 op_sel:[1,1] op_sel_hi:[1,1] neg_hi:[0,1]\n"
         : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
         : "v"(q0), "v"(q1), "v"(q2), "v"(q3));
-    // fp16 sums times fp32 scale, one rounding each
-    asm("v_fma_mix_f32 %0, %8, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
-        "v_fma_mix_f32 %2, %8, %12, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
-        "v_fma_mix_f32 %1, %9, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
-        "v_fma_mix_f32 %3, %9, %12, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
-        "v_fma_mix_f32 %4, %10, %13, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
-        "v_fma_mix_f32 %6, %10, %13, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
-        "v_fma_mix_f32 %5, %11, %13, 0 op_sel:[0,0,0] op_sel_hi:[1,0,0]\n"
-        "v_fma_mix_f32 %7, %11, %13, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n"
+    // fp16 sums times the fp16 scale: exact products in fp32 (at most 16 significant bits)
+    asm("v_fma_mix_f32 %0, %8, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,1,0]\n"
+        "v_fma_mix_f32 %2, %8, %12, 0 op_sel:[1,0,0] op_sel_hi:[1,1,0]\n"
+        "v_fma_mix_f32 %1, %9, %12, 0 op_sel:[0,0,0] op_sel_hi:[1,1,0]\n"
+        "v_fma_mix_f32 %3, %9, %12, 0 op_sel:[1,0,0] op_sel_hi:[1,1,0]\n"
+        "v_fma_mix_f32 %4, %10, %13, 0 op_sel:[0,0,0] op_sel_hi:[1,1,0]\n"
+        "v_fma_mix_f32 %6, %10, %13, 0 op_sel:[1,0,0] op_sel_hi:[1,1,0]\n"
+        "v_fma_mix_f32 %5, %11, %13, 0 op_sel:[0,0,0] op_sel_hi:[1,1,0]\n"
+        "v_fma_mix_f32 %7, %11, %13, 0 op_sel:[1,0,0] op_sel_hi:[1,1,0]\n"
         : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]),
           "=&v"(x[6]), "=&v"(x[7])
-        : "v"(r0), "v"(r1), "v"(r2), "v"(r3), "v"(hs_lo), "v"(hs_hi));
+        : "v"(r0), "v"(r1), "v"(r2), "v"(r3), "v"(s_lo), "v"(s_hi));
     hadamard_cross_lane(x, g);   // stages h = 4..32; x = group_sign(g) * (the row before h = 64)
 #pragma unroll
     for (int m = 0; m < 4; m++) {
@@ -159,11 +154,11 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
     const size_t row0 = (size_t)pair * n_keep + t0;    // chain row of the tile's first token
 
     // queries of this kv head in the key layout of decode_key_split (this lane's dims 4g..4g+3
-    // and 64+4g..64+4g+3), times group_sign(g) / sqrt(128): the keys come out with
-    // group_sign(g) applied, so q . x is the true score
+    // and 64+4g..64+4g+3), times group_sign(g) / 256: the keys come out times
+    // group_sign(g) * 2 sqrt(128), so q . x is the true score q . K / sqrt(128) (exact scaling)
     float qv[G][8];
     {
-        const float f = group_sign(g) * kInvSqrt128;
+        const float f = group_sign(g) * (1.0f / 256.0f);
 #pragma unroll
         for (int i = 0; i < G; i++) {
             const uint16_t *qp = a.Q + ((size_t)lc * a.Hq + h * G + i) * kHeadDim + 4 * g;
@@ -187,32 +182,42 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
                                                    2 * (size_t)pairs, tile,
                                                    a.lb_ticket + kTicketErr);
         const uint16_t *sl = reinterpret_cast<const uint16_t *>(sh.u.t.scale);
-        const float hsf = 0.5f * kInvSqrt128;
+        // the rotary table through buffer resources: a row is 256 bytes at 32-bit offset
+        // p * 256 (positions are below 2^23), the lane's 16 bytes at 16 g within it
+        const __amdgpu_buffer_rsrc_t rcos = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(a.rope_cos), 0, a.T * 256, kBufWord3);
+        const __amdgpu_buffer_rsrc_t rsin = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(a.rope_sin), 0, a.T * 256, kBufWord3);
+        const uint32_t lane_rot = 16u * (uint32_t)g;
+        auto load_rot = [&](int jrow, float c[4], float sn[4]) {
+            const uint32_t o = ((uint32_t)sh.pos[jrow] << 8) | lane_rot;
+            const u32x4 vc = __builtin_amdgcn_raw_buffer_load_b128(rcos, o, 0, 0);
+            const u32x4 vs = __builtin_amdgcn_raw_buffer_load_b128(rsin, o, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                c[k] = __uint_as_float(vc[k]);
+                sn[k] = __uint_as_float(vs[k]);
+            }
+        };
         // Every lane group walks kFusedRun rows. Rows past the tile's end (only in a chain's
         // last, partial tile) are computed on the last row's data and not reported, so the loop
         // has no branch around a load: the rotary rows of token i + kRotAhead are requested while
         // token i is computed, with exact waits.
         float rc[kRotAhead + 1][4], rs[kRotAhead + 1][4];
 #pragma unroll
-        for (int i = 0; i < kRotAhead; i++) {
-            const size_t p = (size_t)sh.pos[min(jl0 + i, nt - 1)] * 64 + 4 * g;
-            load_f32x4(a.rope_cos + p, rc[i]);
-            load_f32x4(a.rope_sin + p, rs[i]);
-        }
+        for (int i = 0; i < kRotAhead; i++) load_rot(min(jl0 + i, nt - 1), rc[i], rs[i]);
 #pragma unroll
         for (int i = 0; i < kFusedRun; i++) {
             const int jl = jl0 + i, jr = min(jl, nt - 1), cur = i % (kRotAhead + 1);
             if (i + kRotAhead < kFusedRun) {
                 const int nx = (i + kRotAhead) % (kRotAhead + 1);
-                const size_t p = (size_t)sh.pos[min(jl + kRotAhead, nt - 1)] * 64 + 4 * g;
-                load_f32x4(a.rope_cos + p, rc[nx]);
-                load_f32x4(a.rope_sin + p, rs[nx]);
+                load_rot(min(jl + kRotAhead, nt - 1), rc[nx], rs[nx]);
             }
             run = run_step(run, lane_delta<true>(sh.u.t.delta, jr, g));
-            const float hs_lo = hsf * h2f(sl[jr * kGroups + (g >> 1)]);
-            const float hs_hi = hsf * h2f(sl[jr * kGroups + 8 + (g >> 1)]);
+            const uint32_t s_lo = sl[jr * kGroups + (g >> 1)];
+            const uint32_t s_hi = sl[jr * kGroups + 8 + (g >> 1)];
             float x[8];
-            decode_key_split(g, run, hs_lo, hs_hi, rc[cur], rs[cur], x);
+            decode_key_split(g, run, s_lo, s_hi, rc[cur], rs[cur], x);
             float d[G];
 #pragma unroll
             for (int hq = 0; hq < G; hq++) {
@@ -252,9 +257,10 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
     }
     __syncthreads();   // also: every key row has been read, the staging area may be reused
 
-    // ---- values: acc[i][k] = sum_t p_t,i * (s_t / 2) * c_t,k, on the codes themselves: each
-    //      code is an exact fp16, and one v_fma_mix_f32 per (head, dim) multiplies it by the
-    //      fp32 weight and adds to the fp32 accumulator with one rounding
+    // ---- values: acc[i][k] = sum_t p_t,i * s_t * c_t,k (twice the dequantised sum; the merge
+    //      halves it), on the codes themselves: each code is an exact fp16, and one
+    //      v_fma_mix_f32 per (head, dim) multiplies it by the fp32 weight and adds to the fp32
+    //      accumulator with one rounding
     stage_tile<kFusedRun>(a.codes_v, a.scales_v, row0, nt, nullptr, a.T, sh.u.t.delta, sh.u.t.scale,
                nullptr);
     float acc[G][8];
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend(FusedArgs a)
         for (int i = 0; i < kFusedRun; i++) {
             const int jl = jl0 + i, jr = min(jl, nt - 1);
             run = run_step(run, sd[jr * 16]);
-            const float hs = 0.5f * h2f(sl[jr * kGroups + g]);
+            const float hs = h2f(sl[jr * kGroups + g]);   // s; the 1/2 is applied in the merge
             const f16x2 c01 = codes_f16(run.x, 0x04010400u), c23 = codes_f16(run.x, 0x04030402u);
             const f16x2 c45 = codes_f16(run.y, 0x04010400u), c67 = codes_f16(run.y, 0x04030402u);
             const float c[8] = {(float)c01.x, (float)c01.y, (float)c23.x, (float)c23.y,
@@ -367,7 +373,8 @@ __global__ __launch_bounds__(kCodecThreads) void k_decode_attend_merge(FusedArgs
         }
     }
     hadamard_butterflies(x, g);   // x = group_sign(g) * H acc
-    const float f = L > 0.0f ? group_sign(g) * kInvSqrt128 / L : 0.0f;
+    // the tiles summed p * s * c: the 1/2 of s / 2 and the 1/sqrt(128) of H (exact scalings)
+    const float f = L > 0.0f ? group_sign(g) * (0.5f * kInvSqrt128) / L : 0.0f;
     float *o = a.out + ((size_t)lc * a.Hq + j) * kHeadDim + 8 * g;
 #pragma unroll
     for (int k = 0; k < 8; k++) o[k] = x[k] * f;
