@@ -36,6 +36,23 @@ CASES = [
 ]
 
 
+def random_cases(n: int = 12, seed: int = 20261204):
+    """Seeded random cases: 1 to ~5000 tokens (log-uniform), windows up to 256, eviction rates
+    including none and all, every group size and bit budget pair, protected layers."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        T = max(1, int(np.exp(rng.uniform(0.0, np.log(5000.0)))))
+        W = int(rng.integers(0, min(T, 256) + 1))
+        e = int(rng.choice([0, 1000, int(rng.integers(1, 1000))], p=[0.1, 0.1, 0.8]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        L = int(rng.integers(1, 4))
+        pb = int(rng.integers(0, 2)) if L == 3 else 0
+        bk, bv = int(rng.integers(2, 5)), int(rng.integers(2, 5))
+        out.append((T, W, e, G, L, pb, bk, bv))
+    return out
+
+
 def oracle_layers(w, T, layers):
     Ct, St = oracle.rope_table(T, w.rope_base)
     encs = []
@@ -46,7 +63,7 @@ def oracle_layers(w, T, layers):
     return encs, Ct, St
 
 
-@pytest.mark.parametrize("T,W,e,G,L,pb,bk,bv", CASES)
+@pytest.mark.parametrize("T,W,e,G,L,pb,bk,bv", CASES + random_cases())
 def test_decode_attend_on_oracle_cache(T, W, e, G, L, pb, bk, bv):
     w = kvsynth.workload(0).with_(tokens=T, window=W, evict_permille=e, layers=L,
                                   protect_boundary=pb, bits_k=bk, bits_v=bv)

@@ -171,6 +171,34 @@ def test_edge_cases(case):
     run_case(w)
 
 
+def random_configs(n: int = 40, seed: int = 20261203):
+    """Seeded random configurations: 1-3 layers (protected layers when there are 3), 1-4 kv
+    heads, 1 to ~20000 tokens (log-uniform), windows up to 400, eviction rates including none
+    and all, every bit budget pair, three RoPE bases and random outlier channels."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        L, H = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        T = max(1, int(np.exp(rng.uniform(0.0, np.log(20000.0)))))
+        W = int(rng.integers(0, min(T, 400) + 1))
+        e = int(rng.choice([0, 1000, int(rng.integers(1, 1000))], p=[0.1, 0.1, 0.8]))
+        bk, bv = int(rng.integers(2, 5)), int(rng.integers(2, 5))
+        base = float(rng.choice([1e4, 5e5, 1e6]))
+        pb = int(rng.integers(0, 2)) if L == 3 else 0
+        kout = (int(rng.integers(0, 9)), float(rng.uniform(1.0, 16.0)))
+        vout = (int(rng.integers(0, 9)), float(rng.uniform(1.0, 16.0)))
+        out.append(kvsynth.Workload(f"random-{i}", L, H, T, W, e, bk, bv, base, kout, vout, pb,
+                                    5000 + i))
+    return out
+
+
+@pytest.mark.parametrize("w", random_configs(), ids=lambda w: w.name)
+def test_random_configs(w):
+    """The whole path against the oracle on seeded random shapes, under the same rules as the
+    edge cases."""
+    run_case(w)
+
+
 def test_repeatable_bitwise():
     """Two runs of the whole path give identical bytes (no races in the look-back scan or the
     selection)."""
