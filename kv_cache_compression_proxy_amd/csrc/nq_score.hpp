@@ -531,7 +531,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
     __shared__ SelectShared sh;
     __shared__ uint32_t s_cnt[kCnt];
     __shared__ uint32_t s_gt[kWords][kSelThreads], s_eq[kWords][kSelThreads];
-    __shared__ uint64_t s_ck[kSelCompact];   // the chosen bucket's keys, once it is small
+    __shared__ uint64_t s_ck[kSelCompact];   // the chosen bucket's keys, once it is small,
+    __shared__ int32_t s_cp[kSelCompact];    // and their positions
     __shared__ uint32_t s_nck;
     const int lc = blockIdx.x;
     const double *s = scores + (size_t)lc * T;
@@ -565,10 +566,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
         sel_init_prefix(sh, kmin, kmax);
     }
     __syncthreads();
+    // Once the chosen bucket holds at most kSelCompact keys, they are gathered into LDS with
+    // their positions and the remaining passes count only them, instead of re-reading every
+    // score per pass. The same read marks the candidates above the bucket (kept whatever the
+    // remaining passes decide), so the flags of the rest come from the gathered keys alone.
+    bool compact = false;
     if (partial) {
-        // Once the chosen bucket holds at most kSelCompact keys, they are gathered into LDS and
-        // the remaining passes count only them, instead of re-reading every score per pass.
-        bool compact = false;
         for (int top = sh.bits; top > 0; top -= 8) {
             const int shift = top >= 8 ? top - 8 : 0;
             const uint32_t dmask = top >= 8 ? 255u : ((1u << top) - 1u);
@@ -603,20 +606,33 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
                 const uint64_t p2 = sh.prefix, m2 = sh.mask;
                 if (tid == 0) s_nck = 0u;
                 __syncthreads();
+                for (int w = 0; w < kWords; w++) {
+                    uint32_t g1 = 0u;
 #pragma unroll 1
-                for (int u0 = 0; u0 < KPT; u0 += kBatch) {
-                    double v[kBatch];
+                    for (int u0 = 0; u0 < 32; u0 += kBatch) {
+                        double v[kBatch];
 #pragma unroll
-                    for (int b = 0; b < kBatch; b++) {
-                        const int t = 1 + tid + (u0 + b) * kSelThreads;
-                        v[b] = t < c_end ? s[t] : 0.0;
-                    }
+                        for (int b = 0; b < kBatch; b++) {
+                            const int t = 1 + tid + (32 * w + u0 + b) * kSelThreads;
+                            v[b] = t < c_end ? s[t] : 0.0;
+                        }
 #pragma unroll
-                    for (int b = 0; b < kBatch; b++) {
-                        const uint64_t k = order_key(v[b]);
-                        if (1 + tid + (u0 + b) * kSelThreads < c_end && (k & m2) == p2)
-                            s_ck[atomicAdd(&s_nck, 1u)] = k;
+                        for (int b = 0; b < kBatch; b++) {
+                            const int t = 1 + tid + (32 * w + u0 + b) * kSelThreads;
+                            if (t < c_end) {
+                                const uint64_t k = order_key(v[b]);
+                                if ((k & m2) > p2) {
+                                    g1 |= 1u << (u0 + b);
+                                } else if ((k & m2) == p2) {
+                                    const uint32_t i = atomicAdd(&s_nck, 1u);
+                                    s_ck[i] = k;
+                                    s_cp[i] = t;
+                                }
+                            }
+                        }
                     }
+                    s_gt[w][tid] = g1;
+                    s_eq[w][tid] = 0u;
                 }
                 __syncthreads();
                 compact = true;
@@ -629,8 +645,20 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
     const uint64_t below = (1ull << lane) - 1ull;
     // bit u of word u / 32: chunk u's candidate is above the selected key (gt) or equal (eq)
     // per-thread flag words in LDS ([word][thread]: conflict-free), so no register array is
-    // indexed by a loop variable
-    for (int w = 0; w < kWords; w++) {
+    // indexed by a loop variable. After a compaction only the gathered keys are left to flag
+    // (the candidate at position t is chunk (t - 1) / kSelThreads of thread (t - 1) %
+    // kSelThreads).
+    if (compact) {
+        const int nck = (int)s_nck;
+        for (int i = tid; i < nck; i += kSelThreads) {
+            const uint64_t k = s_ck[i] & mask;
+            const int t1 = s_cp[i] - 1, th = t1 % kSelThreads, u = t1 / kSelThreads;
+            if (k > prefix) atomicOr(&s_gt[u >> 5][th], 1u << (u & 31));
+            else if (k == prefix) atomicOr(&s_eq[u >> 5][th], 1u << (u & 31));
+        }
+        __syncthreads();
+    }
+    for (int w = 0; w < kWords && !compact; w++) {
         uint32_t g1 = 0u, e1 = 0u;
 #pragma unroll 1
         for (int u0 = 0; u0 < 32; u0 += kBatch) {
