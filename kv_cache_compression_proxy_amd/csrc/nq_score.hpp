@@ -534,6 +534,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
     __shared__ uint64_t s_ck[kSelCompact];   // the chosen bucket's keys, once it is small,
     __shared__ int32_t s_cp[kSelCompact];    // and their positions
     __shared__ uint32_t s_nck;
+    __shared__ uint32_t s_above, s_match;
+    __shared__ int s_retry;
     const int lc = blockIdx.x;
     const double *s = scores + (size_t)lc * T;
     int32_t *out = positions + (size_t)lc * n_keep;
@@ -543,8 +545,36 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
     const int m = n_keep - (T - n_cand);
     const bool partial = m > 0 && m < n_cand;
 
-    if (tid == 0) { sh.prefix = 0ull; sh.mask = 0ull; sh.krem = m; sh.all = 0; sh.bits = 64; }
+    // The radix passes start below the bits that every candidate shares. Those are guessed from
+    // the extremes of a sample (kBatch chunks spread over the layer): the first pass then also
+    // counts the candidates above the guessed range and checks that the m-th best key lies in
+    // it; if it does not (or the sample is flat), the extremes of every candidate are taken as
+    // usual and the passes start over. A correct guess saves one read of the scores.
+    if (tid == 0) {
+        sh.prefix = 0ull; sh.mask = 0ull; sh.krem = m; sh.all = 0; sh.bits = 64;
+        s_above = 0u; s_match = 0u; s_retry = 0;
+    }
+    bool guessed = false;
     if (partial) {
+        uint64_t kmin = ~0ull, kmax = 0ull;
+        double v[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; b++) {
+            const int t = 1 + tid + b * (KPT / kBatch) * kSelThreads;
+            v[b] = t < c_end ? s[t] : 0.0;
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; b++) {
+            if (1 + tid + b * (KPT / kBatch) * kSelThreads < c_end) {
+                const uint64_t k = order_key(v[b]);
+                kmin = k < kmin ? k : kmin;
+                kmax = k > kmax ? k : kmax;
+            }
+        }
+        sel_init_prefix(sh, kmin, kmax);
+        guessed = sh.bits > 0;
+    }
+    auto extremes_pass = [&]() {
         uint64_t kmin = ~0ull, kmax = 0ull;
 #pragma unroll 1
         for (int u0 = 0; u0 < KPT; u0 += kBatch) {
@@ -563,8 +593,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
                 }
             }
         }
+        if (tid == 0) { sh.krem = m; sh.all = 0; }
         sel_init_prefix(sh, kmin, kmax);
-    }
+    };
+    if (partial && !guessed) extremes_pass();
     __syncthreads();
     // Once the chosen bucket holds at most kSelCompact keys, they are gathered into LDS with
     // their positions and the remaining passes count only them, instead of re-reading every
@@ -572,6 +604,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
     // remaining passes decide), so the flags of the rest come from the gathered keys alone.
     bool compact = false;
     if (partial) {
+        bool first = guessed;
         for (int top = sh.bits; top > 0; top -= 8) {
             const int shift = top >= 8 ? top - 8 : 0;
             const uint32_t dmask = top >= 8 ? 255u : ((1u << top) - 1u);
@@ -584,6 +617,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
                     if ((k & mask) == prefix) sel_count(sh, k, shift, dmask);
                 }
             } else {
+                uint32_t above = 0u, match = 0u;
 #pragma unroll 1
                 for (int u0 = 0; u0 < KPT; u0 += kBatch) {
                     double v[kBatch];
@@ -595,8 +629,32 @@ __global__ __launch_bounds__(kSelThreads) void k_select_mem(const double *__rest
 #pragma unroll
                     for (int b = 0; b < kBatch; b++) {
                         const uint64_t k = order_key(v[b]);
-                        if (1 + tid + (u0 + b) * kSelThreads < c_end && (k & mask) == prefix)
-                            sel_count(sh, k, shift, dmask);
+                        if (1 + tid + (u0 + b) * kSelThreads < c_end) {
+                            if ((k & mask) == prefix) {
+                                sel_count(sh, k, shift, dmask);
+                                match++;
+                            } else if ((k & mask) > prefix) {
+                                above++;
+                            }
+                        }
+                    }
+                }
+                if (first) {
+                    // the guessed range: candidates above it are kept, the m-th best must be in it
+                    first = false;
+                    atomicAdd(&s_above, above);
+                    atomicAdd(&s_match, match);
+                    __syncthreads();
+                    if (tid == 0) {
+                        const uint32_t a = s_above;
+                        if (a < (uint32_t)m && (uint32_t)m - a <= s_match) sh.krem = m - (int)a;
+                        else s_retry = 1;
+                    }
+                    __syncthreads();
+                    if (s_retry) {
+                        extremes_pass();
+                        top = sh.bits + 8;   // start over below the true common prefix
+                        continue;
                     }
                 }
             }
