@@ -155,6 +155,10 @@ EDGE = [
     ("select-131073-candidates", 1, 1, 131330, 256, 800, 2, 2, 1e4, 0, 1),
     # zero window over more than 32768 candidates: every score ties (position order decides)
     ("no-window-ties-long", 1, 2, 40000, 0, 600, 3, 2, 1e4, 0, 1),
+    # the long-layer selection at the extremes of the keep rate: the m-th best key near the
+    # largest and near the smallest candidate (beyond a sample's extremes, most likely)
+    ("select-long-keep-few", 1, 2, 40000, 16, 999, 3, 2, 1e4, 0, 1),
+    ("select-long-keep-most", 1, 2, 70000, 16, 1, 3, 2, 1e4, 0, 1),
 ]
 
 
