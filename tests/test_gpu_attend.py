@@ -13,7 +13,14 @@ from gpu_helpers import say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("G,n", [(4, 820), (1, 37), (2, 1), (8, 300), (4, 0)])
+def random_cases(n_cases: int = 8, seed: int = 20261205):
+    """Seeded random (group size, cache length): every group size, 1 to ~5000 tokens."""
+    rng = np.random.default_rng(seed)
+    return [(int(rng.choice([1, 2, 4, 8])), max(1, int(np.exp(rng.uniform(0.0, np.log(5000.0))))))
+            for _ in range(n_cases)]
+
+
+@pytest.mark.parametrize("G,n", [(4, 820), (1, 37), (2, 1), (8, 300), (4, 0)] + random_cases())
 def test_attend_on_oracle_cache(G, n):
     w = kvsynth.workload(0)
     H = w.kv_heads

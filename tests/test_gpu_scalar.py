@@ -103,8 +103,19 @@ def run(T, W, e, bits_k, bits_v, layer=0, rows=None):
     return st
 
 
+def random_cases(n: int = 8, seed: int = 20261206):
+    """Seeded random (tokens, window, eviction, bit budgets): 1 to ~5000 tokens."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        T = max(1, int(np.exp(rng.uniform(0.0, np.log(5000.0)))))
+        out.append((T, int(rng.integers(0, min(T, 300) + 1)), int(rng.integers(0, 1001)),
+                    int(rng.integers(2, 5)), int(rng.integers(2, 5))))
+    return out
+
+
 @pytest.mark.parametrize("T,W,e,bk,bv", [(2048, 128, 600, 3, 2), (700, 50, 400, 4, 2),
-                                         (300, 16, 700, 2, 3), (129, 16, 0, 3, 3)])
+                                         (300, 16, 700, 2, 3), (129, 16, 0, 3, 3)] + random_cases())
 def test_scalar_parity(T, W, e, bk, bv):
     st = run(T, W, e, bk, bv)
     say(f"[scalar] T={T} W={W} e={e} K{bk}V{bv}: {st}")
