@@ -82,7 +82,23 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("T,W,e,G,L,pb", CASES)
+def random_cases(n: int = 8, seed: int = 20261207):
+    """Seeded random cases: 1 to ~4000 tokens, windows up to 300, eviction rates including none
+    and all, every group size, protected layers."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        T = max(1, int(np.exp(rng.uniform(0.0, np.log(4000.0)))))
+        W = int(rng.integers(0, min(T, 300) + 1))
+        e = int(rng.choice([0, 1000, int(rng.integers(1, 1000))], p=[0.1, 0.1, 0.8]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        L = int(rng.integers(1, 4))
+        pb = int(rng.integers(0, 2)) if L == 3 else 0
+        out.append((T, W, e, G, L, pb))
+    return out
+
+
+@pytest.mark.parametrize("T,W,e,G,L,pb", CASES + random_cases())
 def test_attn_score_small(T, W, e, G, L, pb):
     w = kvsynth.workload(0).with_(tokens=T, window=W, evict_permille=e, layers=L,
                                   protect_boundary=pb)
